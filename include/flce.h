@@ -1,0 +1,134 @@
+/*
+ * flce.h -- fused lm_head projection + cross-entropy loss, forward and backward,
+ * for AMD Instinct MI355X (gfx950).  C ABI of libflce.so.
+ *
+ * The operation (for N token rows, hidden size D, vocabulary V):
+ *
+ *   z[n, v]   = sum_d H[n, d] * W[v, d]                 logits, never stored
+ *   lse[n]    = log sum_v exp(z[n, v])                  per-row log-sum-exp
+ *   loss      = (1 / N_valid) * sum_{n valid} (lse[n] - z[n, y[n]])
+ *   dz[n, v]  = (exp(z[n, v] - lse[n]) - [v == y[n]]) * g / N_valid   (valid rows; else 0)
+ *   dH        = dz W,    dW = dz^T H
+ *
+ * The lm_head projection and the loss follow "Arquitectura interna de Unsloth y
+ * optimización en Triton", section 3 (Fused Cross Entropy: the projection Z = X W_vocab^T,
+ * the max-subtracted log-sum-exp, the analytic gradient softmax - onehot, and
+ * backpropagation into both X and W_vocab without writing the logit matrix), and
+ * "Unsloth Architecture: 5x Faster LLM Training via Triton", pillar 1 "Fused Chunked
+ * Cross-Entropy Loss" (the per-row loss -z_y + log sum exp z, its gradient p - onehot,
+ * and the online log-sum-exp over chunks) with its numpy walk-through (mean over
+ * tokens).  A row is valid when its label is not ignore_index; N_valid counts valid rows.
+ * g is the upstream gradient of the loss (1 when grad_loss is NULL).
+ *
+ * Conventions for every call:
+ *  - All tensor pointers are DEVICE pointers on the current HIP device, row-major and
+ *    contiguous: H[N][D], W[V][D] (the nn.Linear weight layout), y[N] int64, lse[N]
+ *    fp32, dH[N][D] in the input element type, dW[V][D] fp32.
+ *  - dtype FLCE_BF16: H, W, dH are bf16 (raw 16-bit patterns); products accumulate in
+ *    fp32; loss, lse and dW are fp32.  dtype FLCE_F32: everything is fp32.
+ *  - The caller owns and allocates every buffer, including the workspace (device
+ *    scratch).  The library allocates nothing, frees nothing and keeps no state between
+ *    calls, so its peak scratch memory is exactly workspace_bytes.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default stream).
+ *    The return value reports only argument and launch errors.  Two calls may run
+ *    concurrently only with distinct workspaces and outputs.
+ *  - Results are deterministic: fixed tile shapes and fixed reduction orders, no
+ *    floating-point atomics; a repeated call with the same inputs and the same
+ *    workspace_bytes produces bitwise-identical outputs.
+ *  - Size limits: 1 <= N, V <= 2^31 - 512, 1 <= D <= 2^31 - 512; D must be a multiple of
+ *    8 (bf16) or 4 (fp32); H, W, dH, dW and workspace must be 16-byte aligned.
+ */
+#ifndef FLCE_H
+#define FLCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum flce_status {
+  FLCE_OK = 0,
+  FLCE_ERR_INVALID_ARG = 1, /* null pointer, size < 1 or too large, unknown dtype */
+  FLCE_ERR_ALIGN = 2,       /* misaligned pointer, or D not a multiple of 8 (bf16) / 4 (fp32) */
+  FLCE_ERR_WORKSPACE = 3,   /* workspace smaller than the call needs */
+  FLCE_ERR_HIP = 4          /* a kernel launch failed (hipGetLastError after launching) */
+} flce_status;
+
+typedef enum flce_dtype {
+  FLCE_F32 = 0,
+  FLCE_BF16 = 1
+} flce_dtype;
+
+/*
+ * Workspace bytes that let both flce_forward and flce_backward run with their default
+ * chunking (the maximum of the two).  Returns 0 for invalid sizes or dtype.
+ *
+ * Forward needs, for T = ceil(V / 256) vocabulary tiles: T * N * 8 bytes of per-tile
+ * (max, sum-exp) partials plus ~12 * N bytes.  Backward needs 12 * N bytes of per-row
+ * state, a dz slab of tc_pad * vc_pad elements of the input type, and (bf16 only) an
+ * fp32 dH accumulator of tc_pad * D floats, where tc_pad and vc_pad are the token and
+ * vocabulary chunk sizes (default min(N, 4096) and min(V, 4096), rounded up to 256).
+ * Every region is rounded up to 256 bytes.
+ */
+size_t flce_workspace_bytes(int64_t N, int64_t D, int64_t V, int dtype);
+
+/*
+ * The chunking flce_backward uses for a workspace of `workspace_bytes`: the largest
+ * (token_chunk, vocab_chunk), multiples of 256, that fit, shrinking the larger of the two
+ * by halves from the default.  Writes them to *token_chunk and *vocab_chunk (either may
+ * be NULL).  Returns FLCE_ERR_WORKSPACE when even 256 x 256 chunks do not fit, and
+ * FLCE_ERR_INVALID_ARG for invalid sizes or dtype.  Host-only; touches no device.
+ * Different chunkings give results that differ only in fp32 summation order.
+ */
+flce_status flce_backward_chunks(int64_t N, int64_t D, int64_t V, int dtype, size_t workspace_bytes,
+                                 int64_t* token_chunk, int64_t* vocab_chunk);
+
+/*
+ * Forward: loss and per-row log-sum-exp without materialising the [N, V] logits.
+ *
+ *   H, W, y        inputs (device), layouts above; y[n] in [0, V) or == ignore_index.
+ *   loss           [1] fp32 out: mean loss over valid rows (0 when N_valid == 0).
+ *   lse            [N] fp32 out: log-sum-exp of every row, ignored rows included
+ *                  (the only per-row state the backward needs besides y).
+ *   n_valid        [1] int32 out: N_valid.
+ *   dev_status     [1] int32 out: 0, or 1 when some label is neither ignore_index nor in
+ *                  [0, V); such rows are then treated as ignored (a precondition
+ *                  violation reported asynchronously; read it after synchronising).
+ *   workspace      device scratch of workspace_bytes bytes (>= the forward's need).
+ *
+ * Errors (synchronous, nothing launched): FLCE_ERR_INVALID_ARG, FLCE_ERR_ALIGN,
+ * FLCE_ERR_WORKSPACE.  FLCE_ERR_HIP if a launch failed.
+ */
+flce_status flce_forward(const void* H, const void* W, const int64_t* y, int64_t N, int64_t D,
+                         int64_t V, int dtype, int64_t ignore_index, float* loss, float* lse,
+                         int32_t* n_valid, int32_t* dev_status, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
+ * Backward: dH and dW from the saved per-row lse, recomputing logit tiles on the fly.
+ *
+ *   H, W, y        the forward's inputs (device).
+ *   lse, n_valid   the forward's outputs (device).
+ *   grad_loss      [1] fp32 device pointer to g = dL_total/dloss, or NULL for g = 1.
+ *   dH             [N][D] out, input element type: overwritten; ignored rows get zeros.
+ *   dW             [V][D] fp32 out: overwritten.
+ *   workspace      device scratch; its size picks the chunking (flce_backward_chunks).
+ *
+ * Labels outside [0, V) that are not ignore_index are treated as ignored (the forward
+ * reports them through dev_status).  Errors as for flce_forward.
+ */
+flce_status flce_backward(const void* H, const void* W, const int64_t* y, const float* lse,
+                          const int32_t* n_valid, const float* grad_loss, int64_t N, int64_t D,
+                          int64_t V, int dtype, int64_t ignore_index, void* dH, float* dW,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* flce_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLCE_H */

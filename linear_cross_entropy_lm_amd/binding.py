@@ -1,0 +1,173 @@
+"""ctypes binding of libflce.so (include/flce.h).  Argument marshalling only: every step
+of the computation runs in the library's HIP kernels; torch provides device memory and
+the current stream.
+
+Importing this module loads the library and raises ImportError if it was not built
+(``python -m linear_cross_entropy_lm_amd.build``); there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflce.so")
+
+FLCE_OK, FLCE_ERR_INVALID_ARG, FLCE_ERR_ALIGN, FLCE_ERR_WORKSPACE, FLCE_ERR_HIP = range(5)
+FLCE_F32, FLCE_BF16 = 0, 1
+IGNORE_INDEX = -100
+
+# symbol -> (restype, argtypes), in the order of include/flce.h
+_P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+SIGNATURES = {
+    "flce_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I32]),
+    "flce_backward_chunks": (_I32, [_I64, _I64, _I64, _I32, _SZ, _P, _P]),
+    "flce_forward": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I32, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
+    "flce_backward": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I64, _P, _P, _P, _SZ, _P]),
+    "flce_status_string": (ctypes.c_char_p, [_I32]),
+}
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m linear_cross_entropy_lm_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    return lib
+
+
+lib = _load()
+
+
+class FlceError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {flce_status_string(code)}")
+        self.code = code
+
+
+def flce_status_string(code: int) -> str:
+    return lib.flce_status_string(int(code)).decode()
+
+
+def dtype_code(dtype: torch.dtype) -> int:
+    if dtype == torch.bfloat16:
+        return FLCE_BF16
+    if dtype == torch.float32:
+        return FLCE_F32
+    raise TypeError(f"unsupported element type {dtype} (bf16 or fp32)")
+
+
+def flce_workspace_bytes(N: int, D: int, V: int, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    return int(lib.flce_workspace_bytes(N, D, V, code))
+
+
+def flce_backward_chunks(N: int, D: int, V: int, dtype, workspace_bytes: int) -> tuple[int, int]:
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    tc, vc = ctypes.c_int64(0), ctypes.c_int64(0)
+    st = lib.flce_backward_chunks(N, D, V, code, workspace_bytes, ctypes.byref(tc), ctypes.byref(vc))
+    if st != FLCE_OK:
+        raise FlceError(st, "flce_backward_chunks")
+    return tc.value, vc.value
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _check(t: torch.Tensor, name: str, dtype: torch.dtype | None = None, shape=None) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def flce_forward(H, W, y, loss, lse, n_valid, dev_status, workspace, ignore_index=IGNORE_INDEX,
+                 stream=None) -> None:
+    """Launch the forward on ``stream`` (default: torch's current stream)."""
+    N, D = H.shape
+    V = W.shape[0]
+    _check(H, "H")
+    _check(W, "W", H.dtype, (V, D))
+    _check(y, "y", torch.int64, (N,))
+    _check(loss, "loss", torch.float32, (1,))
+    _check(lse, "lse", torch.float32, (N,))
+    _check(n_valid, "n_valid", torch.int32, (1,))
+    _check(dev_status, "dev_status", torch.int32, (1,))
+    _check(workspace, "workspace", torch.uint8)
+    st = lib.flce_forward(_ptr(H), _ptr(W), _ptr(y), N, D, V, dtype_code(H.dtype), ignore_index,
+                          _ptr(loss), _ptr(lse), _ptr(n_valid), _ptr(dev_status), _ptr(workspace),
+                          workspace.numel(), _stream(stream))
+    if st != FLCE_OK:
+        raise FlceError(st, "flce_forward")
+
+
+def flce_backward(H, W, y, lse, n_valid, grad_loss, dH, dW, workspace, ignore_index=IGNORE_INDEX,
+                  stream=None) -> None:
+    """Launch the backward on ``stream``; ``grad_loss`` may be None (g = 1)."""
+    N, D = H.shape
+    V = W.shape[0]
+    _check(H, "H")
+    _check(W, "W", H.dtype, (V, D))
+    _check(y, "y", torch.int64, (N,))
+    _check(lse, "lse", torch.float32, (N,))
+    _check(n_valid, "n_valid", torch.int32, (1,))
+    if grad_loss is not None:
+        _check(grad_loss, "grad_loss", torch.float32, (1,))
+    _check(dH, "dH", H.dtype, (N, D))
+    _check(dW, "dW", torch.float32, (V, D))
+    _check(workspace, "workspace", torch.uint8)
+    st = lib.flce_backward(_ptr(H), _ptr(W), _ptr(y), _ptr(lse), _ptr(n_valid), _ptr(grad_loss),
+                           N, D, V, dtype_code(H.dtype), ignore_index, _ptr(dH), _ptr(dW),
+                           _ptr(workspace), workspace.numel(), _stream(stream))
+    if st != FLCE_OK:
+        raise FlceError(st, "flce_backward")
+
+
+class FusedLinearCrossEntropy(torch.autograd.Function):
+    """loss = mean cross-entropy of (H @ W^T, y) with the fused library.  Saves only the
+    per-row lse and N_valid for the backward; dW is returned in fp32."""
+
+    @staticmethod
+    def forward(ctx, H, W, y, ignore_index=IGNORE_INDEX):
+        N, D = H.shape
+        V = W.shape[0]
+        dev = H.device
+        ws = torch.empty(flce_workspace_bytes(N, D, V, H.dtype), dtype=torch.uint8, device=dev)
+        loss = torch.empty(1, dtype=torch.float32, device=dev)
+        lse = torch.empty(N, dtype=torch.float32, device=dev)
+        nv = torch.empty(1, dtype=torch.int32, device=dev)
+        status = torch.empty(1, dtype=torch.int32, device=dev)
+        flce_forward(H, W, y, loss, lse, nv, status, ws, ignore_index)
+        ctx.save_for_backward(H, W, y, lse, nv)
+        ctx.ignore_index = ignore_index
+        return loss[0]
+
+    @staticmethod
+    def backward(ctx, g):
+        H, W, y, lse, nv = ctx.saved_tensors
+        N, D = H.shape
+        V = W.shape[0]
+        ws = torch.empty(flce_workspace_bytes(N, D, V, H.dtype), dtype=torch.uint8, device=H.device)
+        dH = torch.empty_like(H)
+        dW = torch.empty(V, D, dtype=torch.float32, device=H.device)
+        gl = g.reshape(1).to(torch.float32).contiguous()
+        flce_backward(H, W, y, lse, nv, gl, dH, dW, ws, ctx.ignore_index)
+        return dH, dW.to(W.dtype), None, None
+
+
+def fused_linear_cross_entropy(H, W, y, ignore_index=IGNORE_INDEX):
+    return FusedLinearCrossEntropy.apply(H, W, y, ignore_index)

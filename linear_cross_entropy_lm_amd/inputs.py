@@ -11,10 +11,12 @@ Cross-Entropy Logit Disaster": Llama-2 32,000, Mistral 32,768, Llama-3 128,256,
 Qwen-2.5 152,064; a batch of 4 x 4,096 tokens for Llama-3).  No dataset is involved:
 hidden states and weights are Gaussian, labels are uniform or Zipf-skewed.
 
-Generation is blockwise: every 4096-row block of a tensor has its own torch CPU
-generator whose seed is a fixed function of (config seed, tensor id, block index),
-so blocks can be filled in parallel threads and the result does not depend on the
-thread count.
+Generation is blockwise: every 4096-row block of a tensor has its own PCG64 stream
+keyed by (config seed, tensor id, block index), so blocks fill in parallel threads and
+the result does not depend on the thread count.  Normals come from Marsaglia's polar
+method with a log built only from integer steps and correctly rounded + - * / sqrt, and
+bf16 rounding is done on the bit patterns: the bytes are identical on every host CPU
+(library transcendentals and vectorised samplers differ between instruction sets).
 """
 from __future__ import annotations
 
@@ -24,6 +26,15 @@ from dataclasses import dataclass, field, replace
 
 import numpy as np
 import torch
+
+try:  # numpy >= 2
+    from numpy._core.multiarray import _set_madvise_hugepage
+except ImportError:  # pragma: no cover
+    from numpy.core.multiarray import _set_madvise_hugepage
+
+# Large numpy buffers are otherwise madvise'd for transparent huge pages; on hosts where
+# first-touch of such pages is slow this dominates generation time.  Performance only.
+_set_madvise_hugepage(False)
 
 IGNORE_INDEX = -100
 _BLOCK_ROWS = 4096
@@ -86,28 +97,93 @@ def case(N: int, D: int, V: int, dtype: str = "bf16", seed: int = 7, **kw) -> Co
 # bf16 bit-pattern helpers (format conversion only)
 # ---------------------------------------------------------------------------------
 
-def f32_to_bf16_bits(x: torch.Tensor) -> torch.Tensor:
-    """Round-to-nearest-even fp32 -> bf16, returned as int16 bit patterns."""
-    return x.to(torch.bfloat16).view(torch.int16)
-
-
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """Exact widening of bf16 bit patterns (int16/uint16) to fp64."""
     u = bits.view(np.uint16).astype(np.uint32) << 16
     return u.view(np.float32).astype(np.float64)
 
 
-def _block_seed(seed: int, tensor: int, block: int) -> int:
-    return (seed * 1_000_003 + tensor * 10_007 + block * 97 + 12345) % (2**63 - 1)
+_LN2 = 0.6931471805599453
+_SQRT_HALF = 0.7071067811865476
+_LN_TERMS = [1.0 / (2 * k + 1) for k in range(12)]               # 2 atanh series
+_SUB = 1 << 18                                                    # pairs per sub-chunk
 
 
-def _fill_normal(out: torch.Tensor, seed: int, tensor: int, std: float, threads: int) -> None:
-    rows = out.shape[0]
+def _horner(x2: np.ndarray, coefs) -> np.ndarray:
+    acc = np.full_like(x2, coefs[-1])
+    for c in reversed(coefs[:-1]):
+        acc *= x2
+        acc += c
+    return acc
+
+
+def _log(x: np.ndarray) -> np.ndarray:
+    """Natural log of x in (0, 1] from exact frexp plus a 2*atanh series, using only
+    correctly rounded + - * / so the result is identical on every x86 host."""
+    m, e = np.frexp(x)
+    small = m < _SQRT_HALF
+    m = np.where(small, m * 2.0, m)
+    e = np.where(small, e - 1, e).astype(np.float64)
+    t = (m - 1.0) / (m + 1.0)
+    return e * _LN2 + 2.0 * t * _horner(t * t, _LN_TERMS)
+
+
+# Faster log for the sampler: m in [0.5, 1) falls in one of
+# 256 bins of width 1/512 whose centres c_j are exact; ln c_j comes from the series above.
+_LOG_C = 0.5 + (np.arange(256, dtype=np.float64) + 0.5) / 512.0
+_LOG_LNC = _log(_LOG_C)
+
+
+def _log_fast(x: np.ndarray) -> np.ndarray:
+    """ln x for x in (0, 1): ln x = e ln 2 + ln c_j + 2 atanh((m - c_j) / (m + c_j)),
+    |t| < 1e-3 so four series terms reach full double precision."""
+    m, e = np.frexp(x)
+    j = ((m - 0.5) * 512.0).astype(np.int64)
+    c = _LOG_C[j]
+    t = (m - c) / (m + c)
+    t2 = t * t
+    return e * _LN2 + _LOG_LNC[j] + 2.0 * t * (1.0 + t2 * (1.0 / 3.0 + t2 * (1.0 / 5.0 + t2 * (1.0 / 7.0))))
+
+
+def _gaussian_block(seed: int, tensor: int, block: int, rows: int, cols: int) -> np.ndarray:
+    """Standard normals for one row block by Marsaglia's polar method: PCG64 uniform pairs
+    (integer arithmetic) in the unit disc, z = v sqrt(-2 ln s / s), s = |v|^2; accepted
+    pairs fill consecutive elements."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tensor, block])))
+    n = rows * cols
+    need = (n + 1) // 2
+    z = np.empty(2 * need)
+    filled = 0
+    while filled < need:
+        v = rng.random((_SUB, 2)) * 2.0 - 1.0
+        s = v[:, 0] * v[:, 0] + v[:, 1] * v[:, 1]
+        ok = (s > 0.0) & (s < 1.0)
+        v, s = v[ok], s[ok]
+        k = min(len(s), need - filled)
+        v, s = v[:k], s[:k]
+        f = np.sqrt(-2.0 * _log_fast(s) / s)
+        z[2 * filled:2 * (filled + k)] = (v * f[:, None]).reshape(-1)
+        filled += k
+    return z[:n].reshape(rows, cols)
+
+
+def _rne_bf16(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 round-to-nearest-even on the bit patterns (finite inputs), as uint16."""
+    u = x.view(np.uint32)
+    return ((u + (0x7FFF + ((u >> 16) & 1))) >> 16).astype(np.uint16)
+
+
+def _normal_rows(rows: int, cols: int, seed: int, tensor: int, threads: int, finish,
+                 dtype: str) -> np.ndarray:
+    """[rows, cols] of finish(standard normals) rounded to fp32, then (dtype "bf16") to
+    bf16 bit patterns; block b (4096 rows) draws from its own stream."""
+    out = np.empty((rows, cols), dtype=np.float32 if dtype == "f32" else np.uint16)
     nblk = (rows + _BLOCK_ROWS - 1) // _BLOCK_ROWS
 
     def fill(b: int) -> None:
-        g = torch.Generator().manual_seed(_block_seed(seed, tensor, b))
-        out[b * _BLOCK_ROWS:min(rows, (b + 1) * _BLOCK_ROWS)].normal_(0.0, std, generator=g)
+        r0, r1 = b * _BLOCK_ROWS, min(rows, (b + 1) * _BLOCK_ROWS)
+        blk = finish(_gaussian_block(seed, tensor, b, r1 - r0, cols)).astype(np.float32)
+        out[r0:r1] = blk if dtype == "f32" else _rne_bf16(blk)
 
     if nblk == 1 or threads <= 1:
         for b in range(nblk):
@@ -115,6 +191,14 @@ def _fill_normal(out: torch.Tensor, seed: int, tensor: int, std: float, threads:
     else:
         with ThreadPoolExecutor(threads) as ex:
             list(ex.map(fill, range(nblk)))
+    return out
+
+
+def _unit_rms(x: np.ndarray) -> np.ndarray:
+    """Rows scaled to unit root-mean-square (gamma = 1, eps = 0).  The row sum of squares
+    is numpy's pairwise add-reduction: additions only, in a fixed order."""
+    ss = np.add.reduce(x * x, axis=1)
+    return x / np.sqrt(ss / x.shape[1])[:, None]
 
 
 @dataclass
@@ -167,44 +251,59 @@ class Inputs:
 
 
 def generate(cfg: Config, threads: int = 8) -> Inputs:
-    """Draw H, W, labels and the ignore mask (in that order) for ``cfg``."""
+    """Draw H, W, labels and the ignore mask (in that order) for ``cfg``.  Every step is
+    integer arithmetic or correctly rounded floating point, so the bytes are the same on
+    any host."""
     N, D, V = cfg.N, cfg.D, cfg.V
-    H = torch.empty(N, D, dtype=torch.float32)
-    _fill_normal(H, cfg.seed, _TENSOR_H, 1.0, threads)
     if cfg.h_dist == "rms":
-        # unit-RMS rows: h / sqrt(mean(h^2)), gamma = 1, eps = 0, in fp32
-        H.div_(H.square().mean(dim=1, keepdim=True).sqrt_())
-    elif cfg.h_dist != "normal":
+        H = _normal_rows(N, D, cfg.seed, _TENSOR_H, threads, _unit_rms, cfg.dtype)
+    elif cfg.h_dist == "normal":
+        H = _normal_rows(N, D, cfg.seed, _TENSOR_H, threads, lambda z: z, cfg.dtype)
+    else:
         raise ValueError(cfg.h_dist)
-    W = torch.empty(V, D, dtype=torch.float32)
-    _fill_normal(W, cfg.seed, _TENSOR_W, cfg.w_std, threads)
+    W = _normal_rows(V, D, cfg.seed, _TENSOR_W, threads, lambda z: z * cfg.w_std, cfg.dtype)
 
-    g = torch.Generator().manual_seed(_block_seed(cfg.seed, _TENSOR_LABELS, 0))
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg.seed, _TENSOR_LABELS, 0])))
     if cfg.label_dist == "uniform":
-        y = torch.randint(0, V, (N,), generator=g, dtype=torch.int64)
+        y = rng.integers(0, V, size=N, dtype=np.int64)
     elif cfg.label_dist == "zipf":
-        perm = torch.randperm(V, generator=g)
-        ranks = torch.arange(1, V + 1, dtype=torch.float64)
-        p = ranks.pow(-cfg.zipf_s)
-        k = torch.multinomial(p / p.sum(), N, replacement=True, generator=g)
-        y = perm[k]
+        perm = rng.permutation(V)
+        # p_k proportional to k^-s, k = 1..V: weights exp(-s ln k) from the same exact-
+        # arithmetic log, cumulative sum in order, inverse-CDF draw
+        k = np.arange(1, V + 1, dtype=np.float64)
+        m, e = np.frexp(k)  # ln k = ln m + e ln 2 with m in [0.5, 1)
+        lnk = _log(m) + e.astype(np.float64) * _LN2
+        w = _exp_neg(cfg.zipf_s * lnk)
+        cdf = np.cumsum(w)
+        idx = np.searchsorted(cdf, rng.random(N) * cdf[-1], side="right")
+        y = perm[np.minimum(idx, V - 1)].astype(np.int64)
     else:
         raise ValueError(cfg.label_dist)
     k_ign = cfg.n_ignored
     if k_ign:
         if cfg.ignore_layout == "random":
-            idx = torch.randperm(N, generator=g)[:k_ign]
+            idx = rng.permutation(N)[:k_ign]
         elif cfg.ignore_layout == "tail":
-            idx = torch.arange(N - k_ign, N)
+            idx = np.arange(N - k_ign, N)
         else:
             raise ValueError(cfg.ignore_layout)
         y[idx] = IGNORE_INDEX
 
     if cfg.dtype == "bf16":
-        H, W = f32_to_bf16_bits(H), f32_to_bf16_bits(W)
-    elif cfg.dtype != "f32":
+        Ht, Wt = torch.from_numpy(H.view(np.int16)), torch.from_numpy(W.view(np.int16))
+    elif cfg.dtype == "f32":
+        Ht, Wt = torch.from_numpy(H), torch.from_numpy(W)
+    else:
         raise ValueError(cfg.dtype)
-    return Inputs(cfg, H.contiguous(), W.contiguous(), y.contiguous())
+    return Inputs(cfg, Ht.contiguous(), Wt.contiguous(), torch.from_numpy(y).contiguous())
+
+
+def _exp_neg(x: np.ndarray) -> np.ndarray:
+    """exp(-x) for x >= 0 by exact power-of-two reduction and a Taylor series."""
+    n = np.floor(x / _LN2)
+    r = x - n * _LN2                       # in [0, ln 2) up to rounding
+    er = _horner(-r, [1.0 / math.factorial(j) for j in range(20)])
+    return np.ldexp(er, -n.astype(np.int64))
 
 
 def with_labels(inp: Inputs, y: torch.Tensor) -> Inputs:
@@ -214,11 +313,13 @@ def with_labels(inp: Inputs, y: torch.Tensor) -> Inputs:
 
 
 def with_weights_scaled(inp: Inputs, factor: float) -> Inputs:
-    """Same inputs with W multiplied by ``factor`` before rounding (large-logit tests)."""
+    """Same inputs with W multiplied by ``factor`` (in fp32, then rounded to the workload's
+    element type) -- large-logit tests."""
     if inp.cfg.dtype == "f32":
-        W = inp.W * factor
+        W = torch.from_numpy(inp.W.numpy() * np.float32(factor))
     else:
-        W = f32_to_bf16_bits(inp.W.view(torch.bfloat16).float() * factor)
+        w32 = (inp.W.numpy().view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+        W = torch.from_numpy(_rne_bf16(w32 * np.float32(factor)).view(np.int16))
     return Inputs(replace(inp.cfg, name=inp.cfg.name + f"_wx{factor:g}"), inp.H, W.contiguous(),
                   inp.y)
 

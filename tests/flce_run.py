@@ -1,0 +1,70 @@
+"""Test helpers: run the HIP path through the C-ABI binding and compare with the oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+# relative tolerances: (loss, lse max, dH / dW Frobenius)
+TOL = {
+    "f32": dict(loss=1e-5, lse=1e-5, grad=1e-5),
+    "bf16": dict(loss=2e-3, lse=2e-3, grad=1e-2),
+}
+
+
+def run_gpu(inp, g: float | None = None, workspace_bytes: int | None = None,
+            ignore_index: int = -100, device: str = "cuda:0", backward: bool = True) -> dict:
+    """Forward (+ backward) on the device; returns host copies (fp64 numpy for grads)."""
+    from linear_cross_entropy_lm_amd import binding as B
+    H, W, y = inp.device_tensors(device)
+    N, D = H.shape
+    V = W.shape[0]
+    ws_bytes = workspace_bytes or B.flce_workspace_bytes(N, D, V, H.dtype)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
+    loss = torch.empty(1, dtype=torch.float32, device=device)
+    lse = torch.empty(N, dtype=torch.float32, device=device)
+    nv = torch.empty(1, dtype=torch.int32, device=device)
+    status = torch.full((1,), -7, dtype=torch.int32, device=device)
+    B.flce_forward(H, W, y, loss, lse, nv, status, ws, ignore_index)
+    out = dict(loss=float(loss.item()), lse=lse.cpu().double().numpy(), n_valid=int(nv.item()),
+               status=int(status.item()))
+    if backward:
+        dH = torch.full_like(H, float("nan"))
+        dW = torch.full((V, D), float("nan"), dtype=torch.float32, device=device)
+        gl = None if g is None else torch.tensor([g], dtype=torch.float32, device=device)
+        B.flce_backward(H, W, y, lse, nv, gl, dH, dW, ws, ignore_index)
+        torch.cuda.synchronize()
+        out["dH"] = dH.float().cpu().double().numpy()
+        out["dW"] = dW.cpu().double().numpy()
+    torch.cuda.synchronize()
+    return out
+
+
+def rel_fro(a, b) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def compare(got: dict, ref: dict, dtype: str, grads: bool = True) -> dict:
+    """Relative errors of the GPU result against the oracle; asserts the tolerances."""
+    tol = TOL[dtype]
+    err = {}
+    err["loss"] = abs(got["loss"] - ref["loss"]) / max(abs(ref["loss"]), 1e-300)
+    err["lse"] = float(np.max(np.abs(got["lse"] - ref["lse"]) / np.abs(ref["lse"]).clip(1e-30)))
+    assert got["n_valid"] == ref["n_valid"], (got["n_valid"], ref["n_valid"])
+    if ref["n_valid"] == 0:
+        assert got["loss"] == 0.0
+    else:
+        assert err["loss"] <= tol["loss"], err
+    assert err["lse"] <= tol["lse"], err
+    if grads:
+        for k in ("dH", "dW"):
+            assert np.all(np.isfinite(got[k])), f"{k} has non-finite entries"
+            if np.linalg.norm(ref[k]) == 0.0:
+                # exact-zero reference (e.g. V = 1): absolute bound instead of relative
+                err[k] = float(np.max(np.abs(got[k])))
+                assert err[k] <= 1e-6, err
+            else:
+                err[k] = rel_fro(got[k], ref[k])
+                assert err[k] <= tol["grad"], err
+    return err

@@ -1,0 +1,136 @@
+"""Host-only checks of the C ABI: the library loads, exports every function include/flce.h
+declares, and its synchronous argument checks and workspace arithmetic behave as the
+header documents.  Nothing here launches a kernel, so it runs without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flce.h")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from linear_cross_entropy_lm_amd import binding
+    return binding
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(flce_[a-z_]+)\s*\(", text))
+
+
+def test_exports_every_declared_symbol(B):
+    names = _declared()
+    assert names == set(B.SIGNATURES), names ^ set(B.SIGNATURES)
+    raw = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_status_strings(B):
+    for code in range(5):
+        s = B.flce_status_string(code)
+        assert s.startswith(["FLCE_OK", "FLCE_ERR_INVALID_ARG", "FLCE_ERR_ALIGN", "FLCE_ERR_WORKSPACE",
+                             "FLCE_ERR_HIP"][code])
+    assert "unknown" in B.flce_status_string(99)
+
+
+def _r(x, a=256):
+    return (x + a - 1) // a * a
+
+
+def _fwd_bytes(N, V):
+    nvt, nblk = -(-V // 256), -(-N // 256)
+    return _r(nvt * N * 8) + _r(N * 4) + _r(nblk * 8) + 2 * _r(nblk * 4)
+
+
+def _bwd_bytes(N, D, esize, tc, vc, bf16):
+    return 3 * _r(N * 4) + _r(tc * vc * esize) + (_r(tc * D * 4) if bf16 else 0)
+
+
+@pytest.mark.parametrize("N,D,V,dt", [(64, 256, 1024, 0), (4096, 4096, 32000, 1), (8192, 4096, 32768, 1),
+                                      (16384, 4096, 128256, 1), (8192, 3584, 152064, 1), (1, 8, 1, 1),
+                                      (700, 384, 3000, 0)])
+def test_workspace_formula(B, N, D, V, dt):
+    tc, vc = _r(min(N, 4096)), _r(min(V, 4096))
+    esize = 2 if dt == 1 else 4
+    expect = max(_fwd_bytes(N, V), _bwd_bytes(N, D, esize, tc, vc, dt == 1))
+    assert B.flce_workspace_bytes(N, D, V, dt) == expect
+    assert B.flce_backward_chunks(N, D, V, dt, expect) == (tc, vc)
+
+
+def test_llama3_scratch_under_five_percent_of_unfused_logits(B):
+    from linear_cross_entropy_lm_amd.scratch import scratch_fraction, unfused_logit_bytes
+    ws = B.flce_workspace_bytes(16384, 4096, 128256, 1)
+    assert unfused_logit_bytes(16384, 128256) == 4_202_692_608
+    assert scratch_fraction(ws, 16384, 128256) <= 0.05
+
+
+def test_chunk_plan_shrinks_with_workspace(B):
+    N, D, V = 700, 384, 3000
+    full = B.flce_workspace_bytes(N, D, V, 1)
+    plans = []
+    for ws in (full, full // 2, full // 4, full // 8):
+        try:
+            plans.append(B.flce_backward_chunks(N, D, V, 1, ws))
+        except B.FlceError as e:
+            assert e.code == B.FLCE_ERR_WORKSPACE
+            break
+    assert plans[0] == (768, 3072)
+    for (t0, v0), (t1, v1) in zip(plans, plans[1:]):
+        assert t1 <= t0 and v1 <= v0 and (t1, v1) != (t0, v0)
+    for tc, vc in plans:
+        assert tc % 256 == 0 and vc % 256 == 0
+    with pytest.raises(B.FlceError) as e:
+        B.flce_backward_chunks(N, D, V, 1, 1000)
+    assert e.value.code == B.FLCE_ERR_WORKSPACE
+
+
+def test_invalid_sizes(B):
+    assert B.flce_workspace_bytes(0, 8, 8, 1) == 0
+    assert B.flce_workspace_bytes(8, 8, 8, 7) == 0
+    assert B.flce_workspace_bytes(2**31, 8, 8, 1) == 0
+    with pytest.raises(B.FlceError) as e:
+        B.flce_backward_chunks(8, 0, 8, 1, 10**9)
+    assert e.value.code == B.FLCE_ERR_INVALID_ARG
+
+
+# Synchronous error paths with fake (never dereferenced) pointers: the checks run before
+# anything touches the device.
+A16 = 0x10000
+
+
+def _fwd(B, H=A16, W=A16, y=A16, N=8, D=8, V=8, dt=1, loss=A16, lse=A16, nv=A16, st=A16, ws=A16,
+         wsb=10**6):
+    return B.lib.flce_forward(H, W, y, N, D, V, dt, -100, loss, lse, nv, st, ws, wsb, None)
+
+
+def _bwd(B, H=A16, W=A16, y=A16, lse=A16, nv=A16, g=None, N=8, D=8, V=8, dt=1, dH=A16, dW=A16, ws=A16,
+         wsb=10**6):
+    return B.lib.flce_backward(H, W, y, lse, nv, g, N, D, V, dt, -100, dH, dW, ws, wsb, None)
+
+
+def test_forward_argument_errors(B):
+    assert _fwd(B, H=None) == B.FLCE_ERR_INVALID_ARG
+    assert _fwd(B, loss=None) == B.FLCE_ERR_INVALID_ARG
+    assert _fwd(B, ws=None) == B.FLCE_ERR_INVALID_ARG
+    assert _fwd(B, N=0) == B.FLCE_ERR_INVALID_ARG
+    assert _fwd(B, dt=3) == B.FLCE_ERR_INVALID_ARG
+    assert _fwd(B, H=A16 + 8) == B.FLCE_ERR_ALIGN
+    assert _fwd(B, D=12) == B.FLCE_ERR_ALIGN            # bf16 needs D % 8 == 0
+    assert _fwd(B, y=A16 + 4) == B.FLCE_ERR_ALIGN
+    assert _fwd(B, wsb=16) == B.FLCE_ERR_WORKSPACE
+
+
+def test_backward_argument_errors(B):
+    assert _bwd(B, dW=None) == B.FLCE_ERR_INVALID_ARG
+    assert _bwd(B, lse=None) == B.FLCE_ERR_INVALID_ARG
+    assert _bwd(B, V=0) == B.FLCE_ERR_INVALID_ARG
+    assert _bwd(B, dH=A16 + 2) == B.FLCE_ERR_ALIGN
+    assert _bwd(B, dt=0, D=6) == B.FLCE_ERR_ALIGN       # fp32 needs D % 4 == 0
+    assert _bwd(B, g=A16 + 1) == B.FLCE_ERR_ALIGN
+    assert _bwd(B, wsb=100) == B.FLCE_ERR_WORKSPACE
