@@ -79,7 +79,18 @@ def main() -> int:
     ap.add_argument("--workload", default="llama3")
     ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run one device-to-device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        src = torch.ones(args.calibrate_copy // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copied_bytes": args.calibrate_copy}), flush=True)
+        return 0
     if args.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU (asked for {args.gpus}); the multi-GPU "
               "sharding of the path is described, not built.", file=sys.stderr)

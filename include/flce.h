@@ -35,7 +35,7 @@
  *  - Results are deterministic: fixed tile shapes and fixed reduction orders, no
  *    floating-point atomics; a repeated call with the same inputs and the same
  *    workspace_bytes produces bitwise-identical outputs.
- *  - Size limits: 1 <= N, V <= 2^31 - 512, 1 <= D <= 2^31 - 512; D must be a multiple of
+ *  - Size limits: 1 <= N, V <= 2^31 - 512, 1 <= D <= 65536; D must be a multiple of
  *    8 (bf16) or 4 (fp32); H, W, dH, dW and workspace must be 16-byte aligned.
  */
 #ifndef FLCE_H
@@ -69,8 +69,9 @@ typedef enum flce_dtype {
  * (max, sum-exp) partials plus ~12 * N bytes.  Backward needs 12 * N bytes of per-row
  * state, a dz slab of tc_pad * vc_pad elements of the input type, and (bf16 only) an
  * fp32 dH accumulator of tc_pad * D floats, where tc_pad and vc_pad are the token and
- * vocabulary chunk sizes (default min(N, 4096) and min(V, 4096), rounded up to 256).
- * Every region is rounded up to 256 bytes.
+ * vocabulary chunk sizes: by default min(N, 4096) and min(V, 8192) rounded up to 256,
+ * with the vocabulary chunk trimmed in steps of 256 (not below 4096) while the backward
+ * workspace exceeds 5% of N * V * 2 bytes.  Every region is rounded up to 256 bytes.
  */
 size_t flce_workspace_bytes(int64_t N, int64_t D, int64_t V, int dtype);
 

@@ -96,25 +96,49 @@ template <> __device__ __forceinline__ float from_f32<float>(float f) { return f
 // ---------------------------------------------------------------------------------
 // Global -> LDS operand staging.  A tile operand covers kTile rows (r) by one K slice.
 // LDS row r, 16-byte chunk c holds K elements [c * kPerChunk, (c + 1) * kPerChunk).
+// Loads go through buffer descriptors: an offset at or past the descriptor's size reads
+// zeros, so ragged edges need no branches (out-of-range chunks use kOOB).
 // ---------------------------------------------------------------------------------
 
-// Rows K-contiguous in HBM: element (r, k) at p[r * ld + k].  k_lim must be a multiple
-// of kPerChunk so a chunk is either wholly inside or wholly outside.
-template <typename T> struct KContig {
-  static __device__ __forceinline__ void load(u32x4 (&reg)[8], const T* __restrict__ p, int64_t ld,
-                                              int r_lim, int k_lim, int r0, int k0) {
+constexpr u32 kOOB = 0x7ffffff0u;
+
+// Descriptor fields are workgroup-uniform; readfirstlane lets the compiler keep the
+// descriptor in SGPRs instead of looping over lanes around every load.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, u32 bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const u32 lo = __builtin_amdgcn_readfirstlane((u32)a);
+  const u32 hi = __builtin_amdgcn_readfirstlane((u32)(a >> 32));
+  void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, u32 off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+
+// Rows K-contiguous in HBM: tile row r (0..255) starts at base + r * ld_bytes; rows at or
+// beyond rows_ok fall outside the descriptor; K elements at or beyond k_lim are masked
+// (k_lim a multiple of kPerChunk, or the data past it zero, as in the dz slab).
+template <typename T> struct KTile {
+  __amdgpu_buffer_rsrc_t rsrc;
+  u32 voff, rstep;
+  int kc, k_lim;
+  __device__ __forceinline__ KTile(const T* base, int ld_bytes, int rows_ok, int k_lim_) {
     const int t = threadIdx.x;
-    const int k = k0 + (t & 7) * Elem<T>::kPerChunk;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = r0 + i * 32 + (t >> 3);
-      if (r < r_lim && k < k_lim)
-        reg[i] = *reinterpret_cast<const u32x4*>(p + (int64_t)r * ld + k);
-      else
-        reg[i] = u32x4{0u, 0u, 0u, 0u};
-    }
+    const int rows = rows_ok < 0 ? 0 : (rows_ok > kTile ? kTile : rows_ok);
+    rsrc = make_rsrc(base, (u32)rows * (u32)ld_bytes);
+    kc = (t & 7) * Elem<T>::kPerChunk;
+    k_lim = k_lim_;
+    voff = (u32)(t >> 3) * (u32)ld_bytes + (u32)kc * sizeof(T);
+    rstep = 32u * (u32)ld_bytes;
   }
-  static __device__ __forceinline__ void store(const u32x4 (&reg)[8], char* lds) {
+  __device__ __forceinline__ void load(u32x4 (&reg)[8], int k0) const {
+    const bool kok = k0 + kc < k_lim;
+    const u32 o = voff + (u32)k0 * sizeof(T);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) reg[i] = bload(rsrc, kok ? o + (u32)i * rstep : kOOB);
+  }
+  __device__ __forceinline__ void store(const u32x4 (&reg)[8], char* lds) const {
     const int t = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -122,32 +146,34 @@ template <typename T> struct KContig {
   }
 };
 
-// Rows MN-contiguous in HBM: element (r, k) at p[k * ld + r]; r_lim must be a multiple of
-// kPerChunk.  Each thread moves one square block and transposes it in registers.
-template <typename T> struct MNContig;
+// Rows MN-contiguous in HBM: element (tile row c, k) at base + k * ld_bytes + c * sizeof(T)
+// where base is the tile's first column; K rows at or beyond k_lim fall outside the
+// descriptor, tile rows at or beyond cols_ok (a multiple of kPerChunk) are masked.  Each
+// thread moves square blocks and transposes them in registers.
+template <typename T> struct MNTile;
 
-template <> struct MNContig<u16> {
-  // thread t: rows rb = 8 * (t >> 3) .. +7, K elements kb = 8 * (t & 7) .. +7
-  static __device__ __forceinline__ void load(u32x4 (&reg)[8], const u16* __restrict__ p, int64_t ld,
-                                              int r_lim, int k_lim, int r0, int k0) {
+template <> struct MNTile<u16> {
+  // thread t: tile rows cb = 8 * (t >> 3) .. +7, K elements 8 * (t & 7) .. +7
+  __amdgpu_buffer_rsrc_t rsrc;
+  u32 voff, ld;
+  bool cok;
+  __device__ __forceinline__ MNTile(const u16* base, int ld_bytes, int cols_ok, int k_lim) {
     const int t = threadIdx.x;
-    const int r = r0 + (t >> 3) * 8;
-    const int kb = k0 + (t & 7) * 8;
-    const bool rok = r < r_lim;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int k = kb + i;
-      if (rok && k < k_lim)
-        reg[i] = *reinterpret_cast<const u32x4*>(p + (int64_t)k * ld + r);
-      else
-        reg[i] = u32x4{0u, 0u, 0u, 0u};
-    }
+    rsrc = make_rsrc(base, k_lim < 0 ? 0u : (u32)k_lim * (u32)ld_bytes);
+    cok = (t >> 3) * 8 < cols_ok;
+    ld = (u32)ld_bytes;
+    voff = (u32)((t & 7) * 8) * ld + (u32)((t >> 3) * 8) * 2u;
   }
-  // reg[i] = elements (rb + e, kb + i), e = 0..7, two per dword (even e in the low half).
-  // LDS row rb + e gets (rb + e, kb + 0..7): dword m = (kb + 2m, kb + 2m + 1).
-  static __device__ __forceinline__ void store(const u32x4 (&reg)[8], char* lds) {
+  __device__ __forceinline__ void load(u32x4 (&reg)[8], int k0) const {
+    const u32 o = voff + (u32)k0 * ld;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) reg[i] = bload(rsrc, cok ? o + (u32)i * ld : kOOB);
+  }
+  // reg[i] = elements (cb + e, kb + i), e = 0..7, two per dword (even e in the low half).
+  // LDS row cb + e gets (cb + e, kb + 0..7): dword m = (kb + 2m, kb + 2m + 1).
+  __device__ __forceinline__ void store(const u32x4 (&reg)[8], char* lds) const {
     const int t = threadIdx.x;
-    const int rb = (t >> 3) * 8;
+    const int cb = (t >> 3) * 8;
     const int kc = t & 7;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -158,94 +184,129 @@ template <> struct MNContig<u16> {
         const u32 lo = reg[2 * m][h], hi = reg[2 * m + 1][h];
         o[m] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
       }
-      *reinterpret_cast<u32x4*>(lds + (rb + e) * kLdsRow + kc * 16) = o;
+      *reinterpret_cast<u32x4*>(lds + (cb + e) * kLdsRow + kc * 16) = o;
     }
   }
 };
 
-template <> struct MNContig<float> {
-  // two 4 x 4 blocks per thread: block b = t + 256 q, rows 4 * (b >> 3), K 4 * (b & 7)
-  static __device__ __forceinline__ void load(u32x4 (&reg)[8], const float* __restrict__ p, int64_t ld,
-                                              int r_lim, int k_lim, int r0, int k0) {
+template <> struct MNTile<float> {
+  // two 4 x 4 blocks per thread: block b = t + 256 q, tile rows 4 * (b >> 3), K 4 * (b & 7)
+  __amdgpu_buffer_rsrc_t rsrc;
+  u32 voff[2], ld;
+  bool cok[2];
+  __device__ __forceinline__ MNTile(const float* base, int ld_bytes, int cols_ok, int k_lim) {
+    rsrc = make_rsrc(base, k_lim < 0 ? 0u : (u32)k_lim * (u32)ld_bytes);
+    ld = (u32)ld_bytes;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int b = threadIdx.x + kThreads * q;
-      const int r = r0 + (b >> 3) * 4;
-      const int kb = k0 + (b & 7) * 4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int k = kb + i;
-        if (r < r_lim && k < k_lim)
-          reg[q * 4 + i] = *reinterpret_cast<const u32x4*>(p + (int64_t)k * ld + r);
-        else
-          reg[q * 4 + i] = u32x4{0u, 0u, 0u, 0u};
-      }
+      cok[q] = (b >> 3) * 4 < cols_ok;
+      voff[q] = (u32)((b & 7) * 4) * ld + (u32)((b >> 3) * 4) * 4u;
     }
   }
-  static __device__ __forceinline__ void store(const u32x4 (&reg)[8], char* lds) {
+  __device__ __forceinline__ void load(u32x4 (&reg)[8], int k0) const {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const u32 o = voff[q] + (u32)k0 * ld;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) reg[q * 4 + i] = bload(rsrc, cok[q] ? o + (u32)i * ld : kOOB);
+    }
+  }
+  __device__ __forceinline__ void store(const u32x4 (&reg)[8], char* lds) const {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int b = threadIdx.x + kThreads * q;
-      const int rb = (b >> 3) * 4;
+      const int cb = (b >> 3) * 4;
       const int kc = b & 7;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const u32x4 o = {reg[q * 4 + 0][e], reg[q * 4 + 1][e], reg[q * 4 + 2][e], reg[q * 4 + 3][e]};
-        *reinterpret_cast<u32x4*>(lds + (rb + e) * kLdsRow + kc * 16) = o;
+        *reinterpret_cast<u32x4*>(lds + (cb + e) * kLdsRow + kc * 16) = o;
       }
     }
   }
 };
 
 // ---------------------------------------------------------------------------------
-// MFMA over one LDS stage.  32 x 32 block operands: lane l supplies row (l & 31) and the
+// MFMA over LDS stages.  32 x 32 block operands: lane l supplies row (l & 31) and the
 // K elements of 16-byte chunk 2 * ks + (l >> 5).  Result element acc[i][j][r] is
 // C[128 wm + 32 i + 8 (r >> 2) + 4 (l >> 5) + (r & 3)][128 wn + 32 j + (l & 31)].
 // ---------------------------------------------------------------------------------
 
-template <typename T> __device__ __forceinline__ void mfma(f32x16& c, const u32x4& a, const u32x4& b);
-template <> __device__ __forceinline__ void mfma<u16>(f32x16& c, const u32x4& a, const u32x4& b) {
-  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                              __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
+template <typename T> struct Mfma;
+template <> struct Mfma<u16> {
+  static constexpr int kPerFrag = 1;  // MFMA instructions per fragment pair
+  static __device__ __forceinline__ void run(f32x16& c, const u32x4& a, const u32x4& b) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
 // fp32: the four floats of a chunk feed four K = 2 steps; A and B pair the same floats.
 // (Bit-cast the whole fragment, then index: a bit-cast of one vector element reads
 // element 0 under this compiler.)
-template <> __device__ __forceinline__ void mfma<float>(f32x16& c, const u32x4& a, const u32x4& b) {
-  const f32x4 af = __builtin_bit_cast(f32x4, a), bf = __builtin_bit_cast(f32x4, b);
+template <> struct Mfma<float> {
+  static constexpr int kPerFrag = 4;
+  static __device__ __forceinline__ void run(f32x16& c, const u32x4& a, const u32x4& b) {
+    const f32x4 af = __builtin_bit_cast(f32x4, a), bf = __builtin_bit_cast(f32x4, b);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_32x32x2f32(af[e], bf[e], c, 0, 0, 0);
+    for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_32x32x2f32(af[e], bf[e], c, 0, 0, 0);
+  }
+};
+
+__device__ __forceinline__ void read_frags(u32x4 (&fa)[4], u32x4 (&fb)[4], const char* stage, int a_off,
+                                           int b_off, int ks) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const u32x4*>(stage + a_off + i * 32 * kLdsRow + ks * 32);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const u32x4*>(stage + b_off + j * 32 * kLdsRow + ks * 32);
 }
 
 template <typename T>
-__device__ __forceinline__ void mma_stage(f32x16 (&acc)[4][4], const char* As, const char* Bs,
-                                          int wm, int wn, int lane) {
-  const char* pa = As + (wm * kWaveTile + (lane & 31)) * kLdsRow + (lane >> 5) * 16;
-  const char* pb = Bs + (wn * kWaveTile + (lane & 31)) * kLdsRow + (lane >> 5) * 16;
+__device__ __forceinline__ void mma_frags(f32x16 (&acc)[4][4], const u32x4 (&fa)[4], const u32x4 (&fb)[4]) {
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    u32x4 a[4], b[4];
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a[i] = *reinterpret_cast<const u32x4*>(pa + i * 32 * kLdsRow + ks * 32);
-      b[i] = *reinterpret_cast<const u32x4*>(pb + i * 32 * kLdsRow + ks * 32);
-    }
+    for (int j = 0; j < 4; ++j) Mfma<T>::run(acc[i][j], fa[i], fb[j]);
+}
+
+// Scheduling masks for __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100, kSchedDsWrite = 0x200;
+
+// Interleave one K slice's instructions: 64 (x kPerFrag) MFMAs with the next slice's
+// global loads and fragment reads spread over the first three quarters and its LDS
+// stores over the last quarter.
+template <typename T>
+__device__ __forceinline__ void schedule_stage() {
+  constexpr int M = Mfma<T>::kPerFrag;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i) {  // quarter 0: 16 MFMA, 16 global loads, 8 fragment reads
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, M, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, M, 0);
+  }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) mfma<T>(acc[i][j], a[i], b[j]);
+  for (int i = 0; i < 16; ++i) {  // quarters 1-2: 32 MFMA, 16 fragment reads
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, M, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, M, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {  // quarter 3: 16 MFMA, 16 LDS stores
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, M, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
   }
 }
 
-// C[256 x 256] = A[rows a_r0 ..][K] x B[rows b_r0 ..][K]^T over ktiles K slices.
-template <typename T, typename LA, typename LB>
-__device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], char* lds,
-                                          const T* __restrict__ pa, int64_t lda, int a_rlim, int a_klim, int a_r0,
-                                          const T* __restrict__ pb, int64_t ldb, int b_rlim, int b_klim, int b_r0,
-                                          int ktiles) {
+// C[256 x 256] += A[tile rows][K] x B[tile rows][K]^T over ktiles K slices (ktiles >= 1).
+// LDS holds two stages; each iteration loads slice kt + 1 into registers while the MFMAs
+// consume slice kt, with fragments for the next 16-element K step read one step ahead.
+template <typename T, typename TA, typename TB>
+__device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], char* lds, const TA& A, const TB& B, int ktiles) {
   constexpr int BK = kStageK<T>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int a_off = ((wave >> 1) * kWaveTile + (lane & 31)) * kLdsRow + (lane >> 5) * 16;
+  const int b_off = kOperandBytes + ((wave & 1) * kWaveTile + (lane & 31)) * kLdsRow + (lane >> 5) * 16;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -254,26 +315,40 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], char* lds,
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   u32x4 ra[8], rb[8];
-  LA::load(ra, pa, lda, a_rlim, a_klim, a_r0, 0);
-  LB::load(rb, pb, ldb, b_rlim, b_klim, b_r0, 0);
-  LA::store(ra, lds);
-  LB::store(rb, lds + kOperandBytes);
+  u32x4 fa0[4], fb0[4], fa1[4], fb1[4];
+  A.load(ra, 0);
+  B.load(rb, 0);
+  A.store(ra, lds);
+  B.store(rb, lds + kOperandBytes);
   __syncthreads();
-  for (int kt = 0; kt < ktiles; ++kt) {
+  read_frags(fa0, fb0, lds, a_off, b_off, 0);
+  for (int kt = 0; kt + 1 < ktiles; ++kt) {
     const char* cur = lds + (kt & 1) * kStageBytes;
     char* nxt = lds + ((kt + 1) & 1) * kStageBytes;
-    const bool more = kt + 1 < ktiles;
-    if (more) {
-      LA::load(ra, pa, lda, a_rlim, a_klim, a_r0, (kt + 1) * BK);
-      LB::load(rb, pb, ldb, b_rlim, b_klim, b_r0, (kt + 1) * BK);
-    }
-    mma_stage<T>(acc, cur, cur + kOperandBytes, wm, wn, lane);
-    if (more) {
-      LA::store(ra, nxt);
-      LB::store(rb, nxt + kOperandBytes);
-    }
+    A.load(ra, (kt + 1) * BK);
+    B.load(rb, (kt + 1) * BK);
+    read_frags(fa1, fb1, cur, a_off, b_off, 1);
+    mma_frags<T>(acc, fa0, fb0);
+    read_frags(fa0, fb0, cur, a_off, b_off, 2);
+    mma_frags<T>(acc, fa1, fb1);
+    read_frags(fa1, fb1, cur, a_off, b_off, 3);
+    mma_frags<T>(acc, fa0, fb0);
+    mma_frags<T>(acc, fa1, fb1);
+    A.store(ra, nxt);
+    B.store(rb, nxt + kOperandBytes);
+    schedule_stage<T>();
     __syncthreads();
+    read_frags(fa0, fb0, nxt, a_off, b_off, 0);
   }
+  const char* cur = lds + ((ktiles - 1) & 1) * kStageBytes;
+  read_frags(fa1, fb1, cur, a_off, b_off, 1);
+  mma_frags<T>(acc, fa0, fb0);
+  read_frags(fa0, fb0, cur, a_off, b_off, 2);
+  mma_frags<T>(acc, fa1, fb1);
+  read_frags(fa1, fb1, cur, a_off, b_off, 3);
+  mma_frags<T>(acc, fa0, fb0);
+  mma_frags<T>(acc, fa1, fb1);
+  __syncthreads();  // the epilogue may reuse LDS
 }
 
 // ---------------------------------------------------------------------------------
@@ -292,7 +367,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles(const T* __restrict__ H
   const int v0 = vt * kTile, n0 = nt * kTile;
   constexpr int BK = kStageK<T>;
   f32x16 acc[4][4];
-  gemm_tile<T, KContig<T>, KContig<T>>(acc, lds, W, D, V, D, v0, H, D, N, D, n0, (D + BK - 1) / BK);
+  const int ldb = D * (int)sizeof(T);
+  gemm_tile<T>(acc, lds, KTile<T>(W + (int64_t)v0 * D, ldb, V - v0, D), KTile<T>(H + (int64_t)n0 * D, ldb, N - n0, D),
+               (D + BK - 1) / BK);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1, lr = lane & 31, lh = lane >> 5;
@@ -470,8 +547,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dz(const T* __restrict__ H, c
   const int vl0 = vt * kTile, tl0 = tt * kTile;
   constexpr int BK = kStageK<T>;
   f32x16 acc[4][4];
-  gemm_tile<T, KContig<T>, KContig<T>>(acc, lds, W + (int64_t)v0c * D, D, vc_act, D, vl0,
-                                       H + (int64_t)t0c * D, D, tc_act, D, tl0, (D + BK - 1) / BK);
+  const int ldb = D * (int)sizeof(T);
+  gemm_tile<T>(acc, lds, KTile<T>(W + (int64_t)(v0c + vl0) * D, ldb, vc_act - vl0, D),
+               KTile<T>(H + (int64_t)(t0c + tl0) * D, ldb, tc_act - tl0, D), (D + BK - 1) / BK);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1, lr = lane & 31, lh = lane >> 5;
@@ -507,6 +585,62 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dz(const T* __restrict__ H, c
   }
 }
 
+template <typename TO> __device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, u32 off, float v);
+template <> __device__ __forceinline__ void bstore<float>(__amdgpu_buffer_rsrc_t r, u32 off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(u32, v), r, (int)off, 0, 0);
+}
+template <> __device__ __forceinline__ void bstore<u16>(__amdgpu_buffer_rsrc_t r, u32 off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b16((u16)bf16_rne(v), r, (int)off, 0, 0);
+}
+
+// Write a C[row][col] tile held in acc (layout of gemm_tile): out = acc (+ prev when prev
+// is not null).  `prev` (fp32) and `out` point at the tile's first element, both with a
+// row pitch of ld elements; rows at or beyond rows_ok fall outside the buffer descriptors
+// (loads read 0, stores are dropped) and columns at or beyond cols_ok are masked.  The 64
+// previous values of one 32-row band are loaded before any of them is used.
+template <typename TO>
+__device__ __forceinline__ void tile_out(const f32x16 (&acc)[4][4], const float* prev, TO* out, int ld,
+                                         int rows_ok, int cols_ok) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1, lr = lane & 31, lh = lane >> 5;
+  const int rows = rows_ok < kTile ? rows_ok : kTile;
+  const u32 span = (u32)(rows - 1) * (u32)ld + (u32)cols_ok;  // elements inside the tile's range
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(prev ? (const void*)prev : (const void*)out, span * 4u);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(out, span * (u32)sizeof(TO));
+  const u32 lane_row = (u32)(wm * kWaveTile + 4 * lh) * (u32)ld;
+  u32 col[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = wn * kWaveTile + 32 * j + lr;
+    col[j] = c < cols_ok ? lane_row + (u32)c : kOOB;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float pv[4][16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pv[j][r] = 0.f;
+    if (prev) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const u32 e = col[j] == kOOB ? kOOB : (col[j] + (u32)(32 * i + 8 * (r >> 2) + (r & 3)) * (u32)ld) * 4u;
+          pv[j][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rp, (int)e, 0, 0));
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const u32 e = col[j] == kOOB ? kOOB
+                                     : (col[j] + (u32)(32 * i + 8 * (r >> 2) + (r & 3)) * (u32)ld) * (u32)sizeof(TO);
+        bstore<TO>(ro, e, acc[i][j][r] + pv[j][r]);
+      }
+  }
+}
+
 // dH rows of one token chunk += slab x W[vocab chunk]; C[n][d].
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dh(const T* __restrict__ slab, int ld_slab,
@@ -518,30 +652,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh(const T* __restrict__ slab
   const int nl0 = mt * kTile, d0 = dt * kTile;
   constexpr int BK = kStageK<T>;
   f32x16 acc[4][4];
-  gemm_tile<T, KContig<T>, MNContig<T>>(acc, lds, slab, ld_slab, tc_act, vc_act, nl0,
-                                        W + (int64_t)v0c * D, D, D, vc_act, d0, (vc_act + BK - 1) / BK);
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1, lr = lane & 31, lh = lane >> 5;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int d = d0 + wn * kWaveTile + 32 * j + lr;
-    if (d >= D) continue;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int nl = nl0 + wm * kWaveTile + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
-        if (nl >= tc_act) continue;
-        float c = acc[i][j][r];
-        float* pa = dacc + (int64_t)nl * D + d;
-        if (mode & kAccumulate) c += *pa;
-        if (mode & kFinal)
-          dH[(int64_t)(t0c + nl) * D + d] = from_f32<T>(c);
-        else
-          *pa = c;
-      }
-  }
+  const int es = (int)sizeof(T);
+  gemm_tile<T>(acc, lds, KTile<T>(slab + (int64_t)nl0 * ld_slab, ld_slab * es, tc_act - nl0, vc_act),
+               MNTile<T>(W + (int64_t)v0c * D + d0, D * es, D - d0, vc_act), (vc_act + BK - 1) / BK);
+  float* acc_tile = dacc + (int64_t)nl0 * D + d0;
+  const float* prev = (mode & kAccumulate) ? acc_tile : nullptr;
+  if (mode & kFinal)
+    tile_out<T>(acc, prev, dH + (int64_t)(t0c + nl0) * D + d0, D, tc_act - nl0, D - d0);
+  else
+    tile_out<float>(acc, prev, acc_tile, D, tc_act - nl0, D - d0);
 }
 
 // dW rows of one vocab chunk (+)= slab^T x H[token chunk]; C[v][d].
@@ -555,25 +674,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dw(const T* __restrict__ slab
   const int vl0 = mt * kTile, d0 = dt * kTile;
   constexpr int BK = kStageK<T>;
   f32x16 acc[4][4];
-  gemm_tile<T, MNContig<T>, MNContig<T>>(acc, lds, slab, ld_slab, ld_slab, tc_act, vl0,
-                                         H + (int64_t)t0c * D, D, D, tc_act, d0, (tc_act + BK - 1) / BK);
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1, lr = lane & 31, lh = lane >> 5;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int d = d0 + wn * kWaveTile + 32 * j + lr;
-    if (d >= D) continue;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int vl = vl0 + wm * kWaveTile + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
-        if (vl >= vc_act) continue;
-        float* p = dW + (int64_t)(v0c + vl) * D + d;
-        *p = accumulate ? *p + acc[i][j][r] : acc[i][j][r];
-      }
-  }
+  const int es = (int)sizeof(T);
+  gemm_tile<T>(acc, lds, MNTile<T>(slab + vl0, ld_slab * es, ld_slab - vl0, tc_act),
+               MNTile<T>(H + (int64_t)t0c * D + d0, D * es, D - d0, tc_act), (tc_act + BK - 1) / BK);
+  float* tile = dW + (int64_t)(v0c + vl0) * D + d0;
+  tile_out<float>(acc, accumulate ? tile : nullptr, tile, D, vc_act - vl0, D - d0);
 }
 
 // ---------------------------------------------------------------------------------
@@ -581,14 +686,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dw(const T* __restrict__ slab
 // ---------------------------------------------------------------------------------
 
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 512;
-constexpr int64_t kDefaultChunk = 4096;
+constexpr int64_t kMaxHidden = 65536;  // keeps every buffer-descriptor range below 2^31 bytes
+constexpr int64_t kDefaultTokenChunk = 4096;
+constexpr int64_t kDefaultVocabChunk = 8192;
+constexpr int64_t kMinDefaultVocabChunk = 4096;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 inline size_t region(size_t bytes) { return (size_t)round_up((int64_t)bytes, 256); }
 
 bool sizes_ok(int64_t N, int64_t D, int64_t V, int dtype) {
-  return N >= 1 && D >= 1 && V >= 1 && N <= kMaxDim && D <= kMaxDim && V <= kMaxDim &&
+  return N >= 1 && D >= 1 && V >= 1 && N <= kMaxDim && D <= kMaxHidden && V <= kMaxDim &&
          (dtype == FLCE_F32 || dtype == FLCE_BF16);
 }
 
@@ -642,10 +750,22 @@ BwdLayout bwd_layout(int64_t N, int64_t D, int dtype, int64_t tc, int64_t vc) {
   return L;
 }
 
+// Default chunking: token chunk min(N, 4096), vocabulary chunk min(V, 8192), both rounded
+// up to 256; the vocabulary chunk is trimmed in steps of 256 (not below 4096) while the
+// backward workspace exceeds 1/20 of the 16-bit [N, V] logit tensor.
+void default_chunks(int64_t N, int64_t D, int64_t V, int dtype, int64_t* tc_out, int64_t* vc_out) {
+  const int64_t tc = round_up(N < kDefaultTokenChunk ? N : kDefaultTokenChunk, kTile);
+  int64_t vc = round_up(V < kDefaultVocabChunk ? V : kDefaultVocabChunk, kTile);
+  const double cap = 0.05 * 2.0 * (double)N * (double)V;
+  while (vc > kMinDefaultVocabChunk && (double)bwd_layout(N, D, dtype, tc, vc).total > cap) vc -= kTile;
+  *tc_out = tc;
+  *vc_out = vc;
+}
+
 // Largest chunking that fits `ws`, shrinking the larger chunk by halves from the default.
 bool pick_chunks(int64_t N, int64_t D, int64_t V, int dtype, size_t ws, int64_t* tc_out, int64_t* vc_out) {
-  int64_t tc = round_up(N < kDefaultChunk ? N : kDefaultChunk, kTile);
-  int64_t vc = round_up(V < kDefaultChunk ? V : kDefaultChunk, kTile);
+  int64_t tc, vc;
+  default_chunks(N, D, V, dtype, &tc, &vc);
   for (;;) {
     if (bwd_layout(N, D, dtype, tc, vc).total <= ws) {
       *tc_out = tc;
@@ -661,8 +781,8 @@ bool pick_chunks(int64_t N, int64_t D, int64_t V, int dtype, size_t ws, int64_t*
 }
 
 size_t default_bwd_bytes(int64_t N, int64_t D, int64_t V, int dtype) {
-  const int64_t tc = round_up(N < kDefaultChunk ? N : kDefaultChunk, kTile);
-  const int64_t vc = round_up(V < kDefaultChunk ? V : kDefaultChunk, kTile);
+  int64_t tc, vc;
+  default_chunks(N, D, V, dtype, &tc, &vc);
   return bwd_layout(N, D, dtype, tc, vc).total;
 }
 
