@@ -120,6 +120,13 @@ __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, u32 off) {
 // beyond rows_ok fall outside the descriptor; K elements at or beyond k_lim are masked
 // (k_lim a multiple of kPerChunk, or the data past it zero, as in the dz slab).
 template <typename T> struct KTile {
+  static constexpr int kFragReads = 1;
+  static __device__ __forceinline__ int frag_base(int sub, int lane) {
+    return (sub * kWaveTile + (lane & 31)) * kLdsRow + (lane >> 5) * 16;
+  }
+  static __device__ __forceinline__ u32x4 frag(const char* op, int base, int blk, int ks) {
+    return *reinterpret_cast<const u32x4*>(op + base + blk * 32 * kLdsRow + ks * 32);
+  }
   __amdgpu_buffer_rsrc_t rsrc;
   u32 voff, rstep;
   int kc, k_lim;
@@ -148,49 +155,72 @@ template <typename T> struct KTile {
 
 // Rows MN-contiguous in HBM: element (tile row c, k) at base + k * ld_bytes + c * sizeof(T)
 // where base is the tile's first column; K rows at or beyond k_lim fall outside the
-// descriptor, tile rows at or beyond cols_ok (a multiple of kPerChunk) are masked.  Each
-// thread moves square blocks and transposes them in registers.
+// descriptor, tile rows at or beyond cols_ok (a multiple of kPerChunk) are masked.  fp32
+// tiles are transposed in registers before the LDS store; bf16 tiles are stored as they
+// are and transposed by the LDS read.
 template <typename T> struct MNTile;
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// bf16: the K slice is copied into LDS untransposed, as 64 rows k of 256 tile elements
+// (row pitch kTrPitch), and transposed on the way out by ds_read_b64_tr_b16.  Within each
+// 16-lane group that instruction hands lane i the elements i, 16 + i, 32 + i, 48 + i of the
+// group's sixteen 4-element loads; a lane j addressing row k0 + (j >> 2), elements
+// n0 + 4 (j & 3) .. + 3 therefore delivers column n0 + i at rows k0 .. k0 + 3 to lane i, half
+// of a 32 x 32 x 16 MFMA fragment.
+constexpr int kTrPitch = 576;  // 512 bytes of row + 64: four consecutive rows cover 256 bytes of banks
+
 template <> struct MNTile<u16> {
-  // thread t: tile rows cb = 8 * (t >> 3) .. +7, K elements 8 * (t & 7) .. +7
+  static constexpr int kFragReads = 2;
+  // thread t loads 16-byte chunk t & 31 (tile elements 8 (t & 31) .. +7) of K rows (t >> 5) + 8 i
   __amdgpu_buffer_rsrc_t rsrc;
   u32 voff, ld;
   bool cok;
   __device__ __forceinline__ MNTile(const u16* base, int ld_bytes, int cols_ok, int k_lim) {
     const int t = threadIdx.x;
     rsrc = make_rsrc(base, k_lim < 0 ? 0u : (u32)k_lim * (u32)ld_bytes);
-    cok = (t >> 3) * 8 < cols_ok;
+    cok = (t & 31) * 8 < cols_ok;
     ld = (u32)ld_bytes;
-    voff = (u32)((t & 7) * 8) * ld + (u32)((t >> 3) * 8) * 2u;
+    voff = (u32)(t >> 5) * ld + (u32)(t & 31) * 16u;
   }
   __device__ __forceinline__ void load(u32x4 (&reg)[8], int k0) const {
     const u32 o = voff + (u32)k0 * ld;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) reg[i] = bload(rsrc, cok ? o + (u32)i * ld : kOOB);
+    for (int i = 0; i < 8; ++i) reg[i] = bload(rsrc, cok ? o + (u32)(8 * i) * ld : kOOB);
   }
-  // reg[i] = elements (cb + e, kb + i), e = 0..7, two per dword (even e in the low half).
-  // LDS row cb + e gets (cb + e, kb + 0..7): dword m = (kb + 2m, kb + 2m + 1).
   __device__ __forceinline__ void store(const u32x4 (&reg)[8], char* lds) const {
     const int t = threadIdx.x;
-    const int cb = (t >> 3) * 8;
-    const int kc = t & 7;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int h = e >> 1;
-      u32x4 o;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const u32 lo = reg[2 * m][h], hi = reg[2 * m + 1][h];
-        o[m] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-      }
-      *reinterpret_cast<u32x4*>(lds + (cb + e) * kLdsRow + kc * 16) = o;
-    }
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<u32x4*>(lds + ((t >> 5) + 8 * i) * kTrPitch + (t & 31) * 16) = reg[i];
+  }
+  // byte offset, within the operand, of this lane's first fragment read for the 128
+  // tile elements starting at 128 * sub
+  static __device__ __forceinline__ int frag_base(int sub, int lane) {
+    const int g = lane >> 4, j = lane & 15;
+    return (8 * (g >> 1) + (j >> 2)) * kTrPitch + (sub * kWaveTile + 16 * (g & 1) + 4 * (j & 3)) * 2;
+  }
+  // fragment of 32-element block blk (of the 128) and K step ks
+  static __device__ __forceinline__ u32x4 frag(const char* op, int base, int blk, int ks) {
+    char* p = const_cast<char*>(op) + base + blk * 64 + ks * 16 * kTrPitch;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 4 * kTrPitch));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2[0], l2[1], h2[0], h2[1]};
   }
 };
 
 template <> struct MNTile<float> {
-  // two 4 x 4 blocks per thread: block b = t + 256 q, tile rows 4 * (b >> 3), K 4 * (b & 7)
+  // two 4 x 4 blocks per thread: block b = t + 256 q, tile rows 4 * (b >> 3), K 4 * (b & 7);
+  // stored K-contiguous like KTile
+  static constexpr int kFragReads = 1;
+  static __device__ __forceinline__ int frag_base(int sub, int lane) {
+    return (sub * kWaveTile + (lane & 31)) * kLdsRow + (lane >> 5) * 16;
+  }
+  static __device__ __forceinline__ u32x4 frag(const char* op, int base, int blk, int ks) {
+    return *reinterpret_cast<const u32x4*>(op + base + blk * 32 * kLdsRow + ks * 32);
+  }
   __amdgpu_buffer_rsrc_t rsrc;
   u32 voff[2], ld;
   bool cok[2];
@@ -253,12 +283,13 @@ template <> struct Mfma<float> {
   }
 };
 
-__device__ __forceinline__ void read_frags(u32x4 (&fa)[4], u32x4 (&fb)[4], const char* stage, int a_off,
-                                           int b_off, int ks) {
+template <typename TA, typename TB>
+__device__ __forceinline__ void read_frags(u32x4 (&fa)[4], u32x4 (&fb)[4], const char* stage, int a_base,
+                                           int b_base, int ks) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const u32x4*>(stage + a_off + i * 32 * kLdsRow + ks * 32);
+  for (int i = 0; i < 4; ++i) fa[i] = TA::frag(stage, a_base, i, ks);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const u32x4*>(stage + b_off + j * 32 * kLdsRow + ks * 32);
+  for (int j = 0; j < 4; ++j) fb[j] = TB::frag(stage + kOperandBytes, b_base, j, ks);
 }
 
 template <typename T>
@@ -272,41 +303,63 @@ __device__ __forceinline__ void mma_frags(f32x16 (&acc)[4][4], const u32x4 (&fa)
 // Scheduling masks for __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100, kSchedDsWrite = 0x200;
 
-// Interleave one K slice's instructions: 64 (x kPerFrag) MFMAs with the next slice's
-// global loads and fragment reads spread over the first three quarters and its LDS
-// stores over the last quarter.
-template <typename T>
-__device__ __forceinline__ void schedule_stage() {
-  constexpr int M = Mfma<T>::kPerFrag;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {  // quarter 0: 16 MFMA, 16 global loads, 8 fragment reads
+// 16 MFMA groups of M instructions; after group I, the share of R fragment reads, W LDS
+// stores and L global loads that spreads them evenly over the 16 groups.
+template <int M, int R, int W, int L, int I = 0>
+__device__ __forceinline__ void sched_step() {
+  if constexpr (I < 16) {
+    constexpr int r = ((I + 1) * R) / 16 - (I * R) / 16;
+    constexpr int w = ((I + 1) * W) / 16 - (I * W) / 16;
+    constexpr int l = ((I + 1) * L) / 16 - (I * L) / 16;
+    if constexpr (w > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, w, 0);
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, M, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, M, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {  // quarters 1-2: 32 MFMA, 16 fragment reads
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, M, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, M, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {  // quarter 3: 16 MFMA, 16 LDS stores
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, M, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
+    if constexpr (l > 0) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, l, 0);
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, r, 0);
+    sched_step<M, R, W, L, I + 1>();
   }
 }
 
-// C[256 x 256] += A[tile rows][K] x B[tile rows][K]^T over ktiles K slices (ktiles >= 1).
-// LDS holds two stages; each iteration loads slice kt + 1 into registers while the MFMAs
-// consume slice kt, with fragments for the next 16-element K step read one step ahead.
+// One K slice (four 16-element K steps).  On entry the fragments of step 0 of `cur` are in
+// fa0/fb0 and the registers sa/sb hold slice kt + 1 (loaded one slice earlier).  The slice
+// stores sa/sb into `nxt`, starts loading slice kt + 2 into la/lb, runs steps 0-2 reading
+// each next step's fragments one step ahead, synchronises, reads step 0 of `nxt` and runs
+// step 3 on fragments already in registers, so the fragment latency after the barrier is
+// covered by 16 MFMAs.  Loads of slices beyond K read zeros (the descriptors' ranges end).
+template <typename T, typename TA, typename TB>
+__device__ __forceinline__ void gemm_slice(f32x16 (&acc)[4][4], const char* cur, char* nxt, const TA& A,
+                                           const TB& B, u32x4 (&sa)[8], u32x4 (&sb)[8], u32x4 (&la)[8],
+                                           u32x4 (&lb)[8], u32x4 (&fa0)[4], u32x4 (&fb0)[4], u32x4 (&fa1)[4],
+                                           u32x4 (&fb1)[4], int a_base, int b_base, int k_load) {
+  constexpr int M = Mfma<T>::kPerFrag;
+  constexpr int R = 4 * (TA::kFragReads + TB::kFragReads);  // LDS reads per K step
+  A.store(sa, nxt);
+  B.store(sb, nxt + kOperandBytes);
+  A.load(la, k_load);
+  B.load(lb, k_load);
+  read_frags<TA, TB>(fa1, fb1, cur, a_base, b_base, 1);
+  mma_frags<T>(acc, fa0, fb0);
+  read_frags<TA, TB>(fa0, fb0, cur, a_base, b_base, 2);
+  mma_frags<T>(acc, fa1, fb1);
+  read_frags<TA, TB>(fa1, fb1, cur, a_base, b_base, 3);
+  mma_frags<T>(acc, fa0, fb0);
+  sched_step<M, R, 16, 16>();  // step 0 with the LDS stores and global loads
+  sched_step<M, R, 0, 0>();    // step 1
+  sched_step<M, R, 0, 0>();    // step 2
+  __syncthreads();
+  read_frags<TA, TB>(fa0, fb0, nxt, a_base, b_base, 0);
+  mma_frags<T>(acc, fa1, fb1);
+  sched_step<M, R, 0, 0>();    // step 3 under the next slice's first fragment reads
+}
+
+// C[256 x 256] = A[tile rows][K] x B[tile rows][K]^T over ktiles K slices (ktiles >= 1).
+// Two LDS stages and two register staging sets: global loads run two slices ahead of the
+// MFMAs, LDS stores one slice ahead, with one barrier per slice.
 template <typename T, typename TA, typename TB>
 __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], char* lds, const TA& A, const TB& B, int ktiles) {
   constexpr int BK = kStageK<T>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int a_off = ((wave >> 1) * kWaveTile + (lane & 31)) * kLdsRow + (lane >> 5) * 16;
-  const int b_off = kOperandBytes + ((wave & 1) * kWaveTile + (lane & 31)) * kLdsRow + (lane >> 5) * 16;
+  const int a_off = TA::frag_base(wave >> 1, lane);
+  const int b_off = TB::frag_base(wave & 1, lane);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -314,40 +367,24 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], char* lds, const 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  u32x4 ra[8], rb[8];
+  u32x4 a0[8], b0[8], a1[8], b1[8];
   u32x4 fa0[4], fb0[4], fa1[4], fb1[4];
-  A.load(ra, 0);
-  B.load(rb, 0);
-  A.store(ra, lds);
-  B.store(rb, lds + kOperandBytes);
+  A.load(a0, 0);
+  B.load(b0, 0);
+  A.load(a1, BK);
+  B.load(b1, BK);
+  A.store(a0, lds);
+  B.store(b0, lds + kOperandBytes);
   __syncthreads();
-  read_frags(fa0, fb0, lds, a_off, b_off, 0);
-  for (int kt = 0; kt + 1 < ktiles; ++kt) {
-    const char* cur = lds + (kt & 1) * kStageBytes;
-    char* nxt = lds + ((kt + 1) & 1) * kStageBytes;
-    A.load(ra, (kt + 1) * BK);
-    B.load(rb, (kt + 1) * BK);
-    read_frags(fa1, fb1, cur, a_off, b_off, 1);
-    mma_frags<T>(acc, fa0, fb0);
-    read_frags(fa0, fb0, cur, a_off, b_off, 2);
-    mma_frags<T>(acc, fa1, fb1);
-    read_frags(fa1, fb1, cur, a_off, b_off, 3);
-    mma_frags<T>(acc, fa0, fb0);
-    mma_frags<T>(acc, fa1, fb1);
-    A.store(ra, nxt);
-    B.store(rb, nxt + kOperandBytes);
-    schedule_stage<T>();
-    __syncthreads();
-    read_frags(fa0, fb0, nxt, a_off, b_off, 0);
+  read_frags<TA, TB>(fa0, fb0, lds, a_off, b_off, 0);
+  char* s0 = lds;
+  char* s1 = lds + kStageBytes;
+  int kt = 0;
+  for (; kt + 1 < ktiles; kt += 2) {
+    gemm_slice<T>(acc, s0, s1, A, B, a1, b1, a0, b0, fa0, fb0, fa1, fb1, a_off, b_off, (kt + 2) * BK);
+    gemm_slice<T>(acc, s1, s0, A, B, a0, b0, a1, b1, fa0, fb0, fa1, fb1, a_off, b_off, (kt + 3) * BK);
   }
-  const char* cur = lds + ((ktiles - 1) & 1) * kStageBytes;
-  read_frags(fa1, fb1, cur, a_off, b_off, 1);
-  mma_frags<T>(acc, fa0, fb0);
-  read_frags(fa0, fb0, cur, a_off, b_off, 2);
-  mma_frags<T>(acc, fa1, fb1);
-  read_frags(fa1, fb1, cur, a_off, b_off, 3);
-  mma_frags<T>(acc, fa0, fb0);
-  mma_frags<T>(acc, fa1, fb1);
+  if (kt < ktiles) gemm_slice<T>(acc, s0, s1, A, B, a1, b1, a0, b0, fa0, fb0, fa1, fb1, a_off, b_off, (kt + 2) * BK);
   __syncthreads();  // the epilogue may reuse LDS
 }
 
