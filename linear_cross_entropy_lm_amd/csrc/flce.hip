@@ -51,9 +51,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 256;                      // four wave64s
+constexpr int kThreads = 512;                      // eight wave64s, two per SIMD
 constexpr int kTile = 256;                         // output tile edge
-constexpr int kWaveTile = 128;                     // per-wave output edge (2 x 2 waves)
+constexpr int kWaveM = 128, kWaveN = 64;           // per-wave output block (2 x 4 waves)
+constexpr int kBM = kWaveM / 32, kBN = kWaveN / 32;  // 32 x 32 MFMA blocks per wave
 constexpr int kKBytes = 128;                       // K bytes per LDS row per stage
 constexpr int kLdsRow = 144;                       // LDS row pitch in bytes
 constexpr int kOperandBytes = kTile * kLdsRow;     // one operand, one stage
@@ -119,11 +120,14 @@ __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, u32 off) {
 // Rows K-contiguous in HBM: tile row r (0..255) starts at base + r * ld_bytes; rows at or
 // beyond rows_ok fall outside the descriptor; K elements at or beyond k_lim are masked
 // (k_lim a multiple of kPerChunk, or the data past it zero, as in the dz slab).
+// Thread t moves 16-byte chunk t & 7 of rows (t >> 3) + 64 i, i = 0..3.
 template <typename T> struct KTile {
   static constexpr int kFragReads = 1;
-  static __device__ __forceinline__ int frag_base(int sub, int lane) {
-    return (sub * kWaveTile + (lane & 31)) * kLdsRow + (lane >> 5) * 16;
+  // byte offset, within the operand, of this lane's fragment for tile elements elem0 ..
+  static __device__ __forceinline__ int frag_base(int elem0, int lane) {
+    return (elem0 + (lane & 31)) * kLdsRow + (lane >> 5) * 16;
   }
+  // fragment of the 32-element block blk (from elem0) and K step ks
   static __device__ __forceinline__ u32x4 frag(const char* op, int base, int blk, int ks) {
     return *reinterpret_cast<const u32x4*>(op + base + blk * 32 * kLdsRow + ks * 32);
   }
@@ -137,19 +141,19 @@ template <typename T> struct KTile {
     kc = (t & 7) * Elem<T>::kPerChunk;
     k_lim = k_lim_;
     voff = (u32)(t >> 3) * (u32)ld_bytes + (u32)kc * sizeof(T);
-    rstep = 32u * (u32)ld_bytes;
+    rstep = 64u * (u32)ld_bytes;
   }
-  __device__ __forceinline__ void load(u32x4 (&reg)[8], int k0) const {
+  __device__ __forceinline__ void load(u32x4 (&reg)[4], int k0) const {
     const bool kok = k0 + kc < k_lim;
     const u32 o = voff + (u32)k0 * sizeof(T);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) reg[i] = bload(rsrc, kok ? o + (u32)i * rstep : kOOB);
+    for (int i = 0; i < 4; ++i) reg[i] = bload(rsrc, kok ? o + (u32)i * rstep : kOOB);
   }
-  __device__ __forceinline__ void store(const u32x4 (&reg)[8], char* lds) const {
+  __device__ __forceinline__ void store(const u32x4 (&reg)[4], char* lds) const {
     const int t = threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<u32x4*>(lds + (i * 32 + (t >> 3)) * kLdsRow + (t & 7) * 16) = reg[i];
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4*>(lds + (i * 64 + (t >> 3)) * kLdsRow + (t & 7) * 16) = reg[i];
   }
 };
 
@@ -173,7 +177,7 @@ constexpr int kTrPitch = 576;  // 512 bytes of row + 64: four consecutive rows c
 
 template <> struct MNTile<u16> {
   static constexpr int kFragReads = 2;
-  // thread t loads 16-byte chunk t & 31 (tile elements 8 (t & 31) .. +7) of K rows (t >> 5) + 8 i
+  // thread t moves 16-byte chunk t & 31 (tile elements 8 (t & 31) .. +7) of K rows (t >> 5) + 16 i
   __amdgpu_buffer_rsrc_t rsrc;
   u32 voff, ld;
   bool cok;
@@ -184,24 +188,21 @@ template <> struct MNTile<u16> {
     ld = (u32)ld_bytes;
     voff = (u32)(t >> 5) * ld + (u32)(t & 31) * 16u;
   }
-  __device__ __forceinline__ void load(u32x4 (&reg)[8], int k0) const {
+  __device__ __forceinline__ void load(u32x4 (&reg)[4], int k0) const {
     const u32 o = voff + (u32)k0 * ld;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) reg[i] = bload(rsrc, cok ? o + (u32)(8 * i) * ld : kOOB);
+    for (int i = 0; i < 4; ++i) reg[i] = bload(rsrc, cok ? o + (u32)(16 * i) * ld : kOOB);
   }
-  __device__ __forceinline__ void store(const u32x4 (&reg)[8], char* lds) const {
+  __device__ __forceinline__ void store(const u32x4 (&reg)[4], char* lds) const {
     const int t = threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<u32x4*>(lds + ((t >> 5) + 8 * i) * kTrPitch + (t & 31) * 16) = reg[i];
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4*>(lds + ((t >> 5) + 16 * i) * kTrPitch + (t & 31) * 16) = reg[i];
   }
-  // byte offset, within the operand, of this lane's first fragment read for the 128
-  // tile elements starting at 128 * sub
-  static __device__ __forceinline__ int frag_base(int sub, int lane) {
+  static __device__ __forceinline__ int frag_base(int elem0, int lane) {
     const int g = lane >> 4, j = lane & 15;
-    return (8 * (g >> 1) + (j >> 2)) * kTrPitch + (sub * kWaveTile + 16 * (g & 1) + 4 * (j & 3)) * 2;
+    return (8 * (g >> 1) + (j >> 2)) * kTrPitch + (elem0 + 16 * (g & 1) + 4 * (j & 3)) * 2;
   }
-  // fragment of 32-element block blk (of the 128) and K step ks
   static __device__ __forceinline__ u32x4 frag(const char* op, int base, int blk, int ks) {
     char* p = const_cast<char*>(op) + base + blk * 64 + ks * 16 * kTrPitch;
     const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
@@ -212,55 +213,43 @@ template <> struct MNTile<u16> {
 };
 
 template <> struct MNTile<float> {
-  // two 4 x 4 blocks per thread: block b = t + 256 q, tile rows 4 * (b >> 3), K 4 * (b & 7);
-  // stored K-contiguous like KTile
+  // thread t moves the 4 x 4 block of tile rows 4 (t >> 3) .. +3 and K elements 4 (t & 7) .. +3,
+  // transposed, into the K-contiguous layout KTile uses
   static constexpr int kFragReads = 1;
-  static __device__ __forceinline__ int frag_base(int sub, int lane) {
-    return (sub * kWaveTile + (lane & 31)) * kLdsRow + (lane >> 5) * 16;
-  }
+  static __device__ __forceinline__ int frag_base(int elem0, int lane) { return KTile<float>::frag_base(elem0, lane); }
   static __device__ __forceinline__ u32x4 frag(const char* op, int base, int blk, int ks) {
-    return *reinterpret_cast<const u32x4*>(op + base + blk * 32 * kLdsRow + ks * 32);
+    return KTile<float>::frag(op, base, blk, ks);
   }
   __amdgpu_buffer_rsrc_t rsrc;
-  u32 voff[2], ld;
-  bool cok[2];
+  u32 voff, ld;
+  bool cok;
   __device__ __forceinline__ MNTile(const float* base, int ld_bytes, int cols_ok, int k_lim) {
+    const int t = threadIdx.x;
     rsrc = make_rsrc(base, k_lim < 0 ? 0u : (u32)k_lim * (u32)ld_bytes);
     ld = (u32)ld_bytes;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int b = threadIdx.x + kThreads * q;
-      cok[q] = (b >> 3) * 4 < cols_ok;
-      voff[q] = (u32)((b & 7) * 4) * ld + (u32)((b >> 3) * 4) * 4u;
-    }
+    cok = (t >> 3) * 4 < cols_ok;
+    voff = (u32)((t & 7) * 4) * ld + (u32)((t >> 3) * 4) * 4u;
   }
-  __device__ __forceinline__ void load(u32x4 (&reg)[8], int k0) const {
+  __device__ __forceinline__ void load(u32x4 (&reg)[4], int k0) const {
+    const u32 o = voff + (u32)k0 * ld;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const u32 o = voff[q] + (u32)k0 * ld;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) reg[q * 4 + i] = bload(rsrc, cok[q] ? o + (u32)i * ld : kOOB);
-    }
+    for (int i = 0; i < 4; ++i) reg[i] = bload(rsrc, cok ? o + (u32)i * ld : kOOB);
   }
-  __device__ __forceinline__ void store(const u32x4 (&reg)[8], char* lds) const {
+  __device__ __forceinline__ void store(const u32x4 (&reg)[4], char* lds) const {
+    const int t = threadIdx.x;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int b = threadIdx.x + kThreads * q;
-      const int cb = (b >> 3) * 4;
-      const int kc = b & 7;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const u32x4 o = {reg[q * 4 + 0][e], reg[q * 4 + 1][e], reg[q * 4 + 2][e], reg[q * 4 + 3][e]};
-        *reinterpret_cast<u32x4*>(lds + (cb + e) * kLdsRow + kc * 16) = o;
-      }
+    for (int e = 0; e < 4; ++e) {
+      const u32x4 o = {reg[0][e], reg[1][e], reg[2][e], reg[3][e]};
+      *reinterpret_cast<u32x4*>(lds + ((t >> 3) * 4 + e) * kLdsRow + (t & 7) * 16) = o;
     }
   }
 };
 
 // ---------------------------------------------------------------------------------
 // MFMA over LDS stages.  32 x 32 block operands: lane l supplies row (l & 31) and the
-// K elements of 16-byte chunk 2 * ks + (l >> 5).  Result element acc[i][j][r] is
-// C[128 wm + 32 i + 8 (r >> 2) + 4 (l >> 5) + (r & 3)][128 wn + 32 j + (l & 31)].
+// K elements of 16-byte chunk 2 * ks + (l >> 5).  Wave w = 4 wm + wn owns output rows
+// 128 wm .. +127 and columns 64 wn .. +63; its result element acc[i][j][r] is
+// C[128 wm + 32 i + 8 (r >> 2) + 4 (l >> 5) + (r & 3)][64 wn + 32 j + (l & 31)].
 // ---------------------------------------------------------------------------------
 
 template <typename T> struct Mfma;
@@ -284,33 +273,34 @@ template <> struct Mfma<float> {
 };
 
 template <typename TA, typename TB>
-__device__ __forceinline__ void read_frags(u32x4 (&fa)[4], u32x4 (&fb)[4], const char* stage, int a_base,
+__device__ __forceinline__ void read_frags(u32x4 (&fa)[kBM], u32x4 (&fb)[kBN], const char* stage, int a_base,
                                            int b_base, int ks) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) fa[i] = TA::frag(stage, a_base, i, ks);
+  for (int i = 0; i < kBM; ++i) fa[i] = TA::frag(stage, a_base, i, ks);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) fb[j] = TB::frag(stage + kOperandBytes, b_base, j, ks);
+  for (int j = 0; j < kBN; ++j) fb[j] = TB::frag(stage + kOperandBytes, b_base, j, ks);
 }
 
 template <typename T>
-__device__ __forceinline__ void mma_frags(f32x16 (&acc)[4][4], const u32x4 (&fa)[4], const u32x4 (&fb)[4]) {
+__device__ __forceinline__ void mma_frags(f32x16 (&acc)[kBM][kBN], const u32x4 (&fa)[kBM], const u32x4 (&fb)[kBN]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kBM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) Mfma<T>::run(acc[i][j], fa[i], fb[j]);
+    for (int j = 0; j < kBN; ++j) Mfma<T>::run(acc[i][j], fa[i], fb[j]);
 }
 
 // Scheduling masks for __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100, kSchedDsWrite = 0x200;
 
-// 16 MFMA groups of M instructions; after group I, the share of R fragment reads, W LDS
-// stores and L global loads that spreads them evenly over the 16 groups.
+// kBM * kBN MFMA groups of M instructions; after group I, the share of R fragment reads,
+// W LDS stores and L global loads that spreads them evenly over the groups.
 template <int M, int R, int W, int L, int I = 0>
 __device__ __forceinline__ void sched_step() {
-  if constexpr (I < 16) {
-    constexpr int r = ((I + 1) * R) / 16 - (I * R) / 16;
-    constexpr int w = ((I + 1) * W) / 16 - (I * W) / 16;
-    constexpr int l = ((I + 1) * L) / 16 - (I * L) / 16;
+  constexpr int G = kBM * kBN;
+  if constexpr (I < G) {
+    constexpr int r = ((I + 1) * R) / G - (I * R) / G;
+    constexpr int w = ((I + 1) * W) / G - (I * W) / G;
+    constexpr int l = ((I + 1) * L) / G - (I * L) / G;
     if constexpr (w > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, w, 0);
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, M, 0);
     if constexpr (l > 0) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, l, 0);
@@ -319,19 +309,23 @@ __device__ __forceinline__ void sched_step() {
   }
 }
 
+typedef u32x4 Stage4[4];  // one thread's share of one operand's K slice
+
 // One K slice (four 16-element K steps).  On entry the fragments of step 0 of `cur` are in
 // fa0/fb0 and the registers sa/sb hold slice kt + 1 (loaded one slice earlier).  The slice
 // stores sa/sb into `nxt`, starts loading slice kt + 2 into la/lb, runs steps 0-2 reading
 // each next step's fragments one step ahead, synchronises, reads step 0 of `nxt` and runs
 // step 3 on fragments already in registers, so the fragment latency after the barrier is
-// covered by 16 MFMAs.  Loads of slices beyond K read zeros (the descriptors' ranges end).
+// covered by MFMAs.  Loads of slices beyond K read zeros (the descriptors' ranges end).
+// Two waves share each SIMD; a wave raises its priority once past the barrier so the
+// matrix core keeps being fed while its partner finishes the previous slice.
 template <typename T, typename TA, typename TB>
-__device__ __forceinline__ void gemm_slice(f32x16 (&acc)[4][4], const char* cur, char* nxt, const TA& A,
-                                           const TB& B, u32x4 (&sa)[8], u32x4 (&sb)[8], u32x4 (&la)[8],
-                                           u32x4 (&lb)[8], u32x4 (&fa0)[4], u32x4 (&fb0)[4], u32x4 (&fa1)[4],
-                                           u32x4 (&fb1)[4], int a_base, int b_base, int k_load) {
+__device__ __forceinline__ void gemm_slice(f32x16 (&acc)[kBM][kBN], const char* cur, char* nxt, const TA& A,
+                                           const TB& B, Stage4& sa, Stage4& sb, Stage4& la, Stage4& lb,
+                                           u32x4 (&fa0)[kBM], u32x4 (&fb0)[kBN], u32x4 (&fa1)[kBM],
+                                           u32x4 (&fb1)[kBN], int a_base, int b_base, int k_load) {
   constexpr int M = Mfma<T>::kPerFrag;
-  constexpr int R = 4 * (TA::kFragReads + TB::kFragReads);  // LDS reads per K step
+  constexpr int R = kBM * TA::kFragReads + kBN * TB::kFragReads;  // LDS reads per K step
   A.store(sa, nxt);
   B.store(sb, nxt + kOperandBytes);
   A.load(la, k_load);
@@ -342,33 +336,36 @@ __device__ __forceinline__ void gemm_slice(f32x16 (&acc)[4][4], const char* cur,
   mma_frags<T>(acc, fa1, fb1);
   read_frags<TA, TB>(fa1, fb1, cur, a_base, b_base, 3);
   mma_frags<T>(acc, fa0, fb0);
-  sched_step<M, R, 16, 16>();  // step 0 with the LDS stores and global loads
-  sched_step<M, R, 0, 0>();    // step 1
-  sched_step<M, R, 0, 0>();    // step 2
+  sched_step<M, R, 8, 8>();  // step 0 with the LDS stores and global loads
+  sched_step<M, R, 0, 0>();  // step 1
+  sched_step<M, R, 0, 0>();  // step 2
+  __builtin_amdgcn_s_setprio(0);
   __syncthreads();
+  __builtin_amdgcn_s_setprio(1);
   read_frags<TA, TB>(fa0, fb0, nxt, a_base, b_base, 0);
   mma_frags<T>(acc, fa1, fb1);
-  sched_step<M, R, 0, 0>();    // step 3 under the next slice's first fragment reads
+  sched_step<M, R, 0, 0>();  // step 3 under the next slice's first fragment reads
 }
 
 // C[256 x 256] = A[tile rows][K] x B[tile rows][K]^T over ktiles K slices (ktiles >= 1).
 // Two LDS stages and two register staging sets: global loads run two slices ahead of the
 // MFMAs, LDS stores one slice ahead, with one barrier per slice.
 template <typename T, typename TA, typename TB>
-__device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], char* lds, const TA& A, const TB& B, int ktiles) {
+__device__ __forceinline__ void gemm_tile(f32x16 (&acc)[kBM][kBN], char* lds, const TA& A, const TB& B,
+                                          int ktiles) {
   constexpr int BK = kStageK<T>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int a_off = TA::frag_base(wave >> 1, lane);
-  const int b_off = TB::frag_base(wave & 1, lane);
+  const int a_off = TA::frag_base((wave >> 2) * kWaveM, lane);
+  const int b_off = TB::frag_base((wave & 3) * kWaveN, lane);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kBM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kBN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  u32x4 a0[8], b0[8], a1[8], b1[8];
-  u32x4 fa0[4], fb0[4], fa1[4], fb1[4];
+  Stage4 a0, b0, a1, b1;
+  u32x4 fa0[kBM], fb0[kBN], fa1[kBM], fb1[kBN];
   A.load(a0, 0);
   B.load(b0, 0);
   A.load(a1, BK);
@@ -385,6 +382,7 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], char* lds, const 
     gemm_slice<T>(acc, s1, s0, A, B, a0, b0, a1, b1, fa0, fb0, fa1, fb1, a_off, b_off, (kt + 3) * BK);
   }
   if (kt < ktiles) gemm_slice<T>(acc, s0, s1, A, B, a1, b1, a0, b0, fa0, fb0, fa1, fb1, a_off, b_off, (kt + 2) * BK);
+  __builtin_amdgcn_s_setprio(0);
   __syncthreads();  // the epilogue may reuse LDS
 }
 
@@ -403,25 +401,25 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles(const T* __restrict__ H
   const int nt = blockIdx.x % n_tiles_n, vt = blockIdx.x / n_tiles_n;
   const int v0 = vt * kTile, n0 = nt * kTile;
   constexpr int BK = kStageK<T>;
-  f32x16 acc[4][4];
+  f32x16 acc[kBM][kBN];
   const int ldb = D * (int)sizeof(T);
   gemm_tile<T>(acc, lds, KTile<T>(W + (int64_t)v0 * D, ldb, V - v0, D), KTile<T>(H + (int64_t)n0 * D, ldb, N - n0, D),
                (D + BK - 1) / BK);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1, lr = lane & 31, lh = lane >> 5;
-  const int vbase = v0 + wm * kWaveTile + 4 * lh;  // vocab row of acc[0][j][0] in this lane
-  const int vlim = V - vbase;                      // offsets below vlim are real rows
-  float mrow[4], srow[4];
+  const int wm = wave >> 2, wn = wave & 3, lr = lane & 31, lh = lane >> 5;
+  const int vbase = v0 + wm * kWaveM + 4 * lh;  // vocab row of acc[0][j][0] in this lane
+  const int vlim = V - vbase;                   // offsets below vlim are real rows
+  float mrow[kBN], srow[kBN];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + wn * kWaveTile + 32 * j + lr;
+  for (int j = 0; j < kBN; ++j) {
+    const int n = n0 + wn * kWaveN + 32 * j + lr;
     const int64_t lab = n < N ? y[n] : -1;
     const int64_t rel = lab - vbase;
     float m = -__builtin_inff(), zl = 0.f;
     bool hit = false;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kBM; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int off = 32 * i + 8 * (r >> 2) + (r & 3);
@@ -436,7 +434,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles(const T* __restrict__ H
     if (m != -__builtin_inff()) {
       const float mb = m * kLog2e;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kBM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int off = 32 * i + 8 * (r >> 2) + (r & 3);
@@ -452,11 +450,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles(const T* __restrict__ H
   float2* red = reinterpret_cast<float2*>(lds);  // [wm][token in tile]
   if (lh == 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) red[wm * kTile + wn * kWaveTile + 32 * j + lr] = make_float2(mrow[j], srow[j]);
+    for (int j = 0; j < kBN; ++j) red[wm * kTile + wn * kWaveN + 32 * j + lr] = make_float2(mrow[j], srow[j]);
   }
   __syncthreads();
   const int t = threadIdx.x;
-  if (n0 + t < N) {
+  if (t < kTile && n0 + t < N) {
     float m = red[t].x, s = red[t].y;
     lse_merge(m, s, red[kTile + t].x, red[kTile + t].y);
     part[(int64_t)vt * N + n0 + t] = make_float2(m, s);
@@ -583,18 +581,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dz(const T* __restrict__ H, c
   const int tt = blockIdx.x % n_tiles_t, vt = blockIdx.x / n_tiles_t;
   const int vl0 = vt * kTile, tl0 = tt * kTile;
   constexpr int BK = kStageK<T>;
-  f32x16 acc[4][4];
+  f32x16 acc[kBM][kBN];
   const int ldb = D * (int)sizeof(T);
   gemm_tile<T>(acc, lds, KTile<T>(W + (int64_t)(v0c + vl0) * D, ldb, vc_act - vl0, D),
                KTile<T>(H + (int64_t)(t0c + tl0) * D, ldb, tc_act - tl0, D), (D + BK - 1) / BK);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1, lr = lane & 31, lh = lane >> 5;
-  const int vb = vl0 + wm * kWaveTile + 4 * lh;  // chunk-local vocab row of acc[0][j][0]
+  const int wm = wave >> 2, wn = wave & 3, lr = lane & 31, lh = lane >> 5;
+  const int vb = vl0 + wm * kWaveM + 4 * lh;  // chunk-local vocab row of acc[0][j][0]
   const int vlim = vc_act - vb;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int nl = tl0 + wn * kWaveTile + 32 * j + lr;
+  for (int j = 0; j < kBN; ++j) {
+    const int nl = tl0 + wn * kWaveN + 32 * j + lr;
     float L2 = 0.f, cf = 0.f;
     int rel = -1;
     if (nl < tc_act) {
@@ -606,7 +604,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dz(const T* __restrict__ H, c
     }
     T* out = slab + (int64_t)nl * ld_slab + vb;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kBM; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float d[4];
@@ -633,34 +631,34 @@ template <> __device__ __forceinline__ void bstore<u16>(__amdgpu_buffer_rsrc_t r
 // Write a C[row][col] tile held in acc (layout of gemm_tile): out = acc (+ prev when prev
 // is not null).  `prev` (fp32) and `out` point at the tile's first element, both with a
 // row pitch of ld elements; rows at or beyond rows_ok fall outside the buffer descriptors
-// (loads read 0, stores are dropped) and columns at or beyond cols_ok are masked.  The 64
+// (loads read 0, stores are dropped) and columns at or beyond cols_ok are masked.  The
 // previous values of one 32-row band are loaded before any of them is used.
 template <typename TO>
-__device__ __forceinline__ void tile_out(const f32x16 (&acc)[4][4], const float* prev, TO* out, int ld,
+__device__ __forceinline__ void tile_out(const f32x16 (&acc)[kBM][kBN], const float* prev, TO* out, int ld,
                                          int rows_ok, int cols_ok) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1, lr = lane & 31, lh = lane >> 5;
+  const int wm = wave >> 2, wn = wave & 3, lr = lane & 31, lh = lane >> 5;
   const int rows = rows_ok < kTile ? rows_ok : kTile;
   const u32 span = (u32)(rows - 1) * (u32)ld + (u32)cols_ok;  // elements inside the tile's range
   const __amdgpu_buffer_rsrc_t rp = make_rsrc(prev ? (const void*)prev : (const void*)out, span * 4u);
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(out, span * (u32)sizeof(TO));
-  const u32 lane_row = (u32)(wm * kWaveTile + 4 * lh) * (u32)ld;
-  u32 col[4];
+  const u32 lane_row = (u32)(wm * kWaveM + 4 * lh) * (u32)ld;
+  u32 col[kBN];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = wn * kWaveTile + 32 * j + lr;
+  for (int j = 0; j < kBN; ++j) {
+    const int c = wn * kWaveN + 32 * j + lr;
     col[j] = c < cols_ok ? lane_row + (u32)c : kOOB;
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float pv[4][16];
+  for (int i = 0; i < kBM; ++i) {
+    float pv[kBN][16];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kBN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) pv[j][r] = 0.f;
     if (prev) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < kBN; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const u32 e = col[j] == kOOB ? kOOB : (col[j] + (u32)(32 * i + 8 * (r >> 2) + (r & 3)) * (u32)ld) * 4u;
@@ -668,7 +666,7 @@ __device__ __forceinline__ void tile_out(const f32x16 (&acc)[4][4], const float*
         }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kBN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const u32 e = col[j] == kOOB ? kOOB
@@ -688,7 +686,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh(const T* __restrict__ slab
   const int dt = blockIdx.x % n_tiles_d, mt = blockIdx.x / n_tiles_d;
   const int nl0 = mt * kTile, d0 = dt * kTile;
   constexpr int BK = kStageK<T>;
-  f32x16 acc[4][4];
+  f32x16 acc[kBM][kBN];
   const int es = (int)sizeof(T);
   gemm_tile<T>(acc, lds, KTile<T>(slab + (int64_t)nl0 * ld_slab, ld_slab * es, tc_act - nl0, vc_act),
                MNTile<T>(W + (int64_t)v0c * D + d0, D * es, D - d0, vc_act), (vc_act + BK - 1) / BK);
@@ -710,7 +708,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dw(const T* __restrict__ slab
   const int dt = blockIdx.x % n_tiles_d, mt = blockIdx.x / n_tiles_d;
   const int vl0 = mt * kTile, d0 = dt * kTile;
   constexpr int BK = kStageK<T>;
-  f32x16 acc[4][4];
+  f32x16 acc[kBM][kBN];
   const int es = (int)sizeof(T);
   gemm_tile<T>(acc, lds, MNTile<T>(slab + vl0, ld_slab * es, ld_slab - vl0, tc_act),
                MNTile<T>(H + (int64_t)t0c * D + d0, D * es, D - d0, tc_act), (tc_act + BK - 1) / BK);
