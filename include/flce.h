@@ -65,8 +65,9 @@ typedef enum flce_dtype {
  * Workspace bytes that let both flce_forward and flce_backward run with their default
  * chunking (the maximum of the two).  Returns 0 for invalid sizes or dtype.
  *
- * Forward needs, for T = ceil(V / 256) vocabulary tiles: T * N * 8 bytes of per-tile
- * (max, sum-exp) partials plus ~12 * N bytes.  Backward needs 12 * N bytes of per-row
+ * Forward needs S * N * 8 bytes of (max, sum-exp) partials plus ~4 * N bytes, where
+ * S = min(max(256 / ceil(N / 256), 1), ceil(V / 256)) (integer division) is the number
+ * of workgroups that share one 256-row token tile.  Backward needs 12 * N bytes of per-row
  * state, a dz slab of tc_pad * vc_pad elements of the input type, and (bf16 only) an
  * fp32 dH accumulator of tc_pad * D floats, where tc_pad and vc_pad are the token and
  * vocabulary chunk sizes: by default min(N, 4096) and min(V, 8192) rounded up to 256,

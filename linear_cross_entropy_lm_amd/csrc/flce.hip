@@ -62,8 +62,6 @@ constexpr int kStageBytes = 2 * kOperandBytes;     // A and B
 constexpr int kLdsBytes = 2 * kStageBytes;         // two stages: 147456 of 163840
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kAccumulate = 1;                     // epilogue reads the previous partial
-constexpr int kFinal = 2;                          // epilogue writes the converted output
 
 template <typename T> struct Elem;
 template <> struct Elem<u16> { static constexpr int kPerChunk = 8; };    // bf16 bits
@@ -347,121 +345,188 @@ __device__ __forceinline__ void gemm_slice(f32x16 (&acc)[kBM][kBN], const char* 
   sched_step<M, R, 0, 0>();  // step 3 under the next slice's first fragment reads
 }
 
-// C[256 x 256] = A[tile rows][K] x B[tile rows][K]^T over ktiles K slices (ktiles >= 1).
-// Two LDS stages and two register staging sets: global loads run two slices ahead of the
-// MFMAs, LDS stores one slice ahead, with one barrier per slice.
-template <typename T, typename TA, typename TB>
-__device__ __forceinline__ void gemm_tile(f32x16 (&acc)[kBM][kBN], char* lds, const TA& A, const TB& B,
-                                          int ktiles) {
-  constexpr int BK = kStageK<T>;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int a_off = TA::frag_base((wave >> 2) * kWaveM, lane);
-  const int b_off = TB::frag_base((wave & 3) * kWaveN, lane);
+// The two operands of one output tile.
+template <typename A_, typename B_> struct Ops {
+  using TA = A_;
+  using TB = B_;
+  A_ a;
+  B_ b;
+};
+
+template <typename AccT> __device__ __forceinline__ void zero_acc(AccT& acc) {
 #pragma unroll
   for (int i = 0; i < kBM; ++i)
 #pragma unroll
     for (int j = 0; j < kBN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+}
+
+// Persistent GEMM driver.  The workgroup computes `count` >= 1 output tiles of 256 x 256,
+// C = A[tile rows][K] x B[tile rows][K]^T over ktiles K slices each (ktiles even: callers
+// round up, the extra slice reading zeros past K); mk(i) returns the
+// operands of its i-th tile and epi(i, acc) consumes that tile's accumulators.  Two LDS
+// stages and two register staging sets: global loads run two K slices ahead of the MFMAs
+// and LDS stores one slice ahead, with one barrier per slice.  The load stream runs across
+// tile boundaries (the first slices of tile i + 1 load while tile i finishes), so only the
+// epilogue separates consecutive tiles' MFMAs.  Loads past the last tile read zeros.
+template <typename T, typename MakeOps, typename Epi>
+__device__ __forceinline__ void gemm_run(char* lds, int count, int ktiles, const MakeOps& mk, Epi&& epi) {
+  using O = decltype(mk(0));
+  using TA = typename O::TA;
+  using TB = typename O::TB;
+  constexpr int BK = kStageK<T>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int a_off = TA::frag_base((wave >> 2) * kWaveM, lane);
+  const int b_off = TB::frag_base((wave & 3) * kWaveN, lane);
+  f32x16 acc[kBM][kBN];
+  zero_acc(acc);
 
   Stage4 a0, b0, a1, b1;
   u32x4 fa0[kBM], fb0[kBN], fa1[kBM], fb1[kBN];
-  A.load(a0, 0);
-  B.load(b0, 0);
-  A.load(a1, BK);
-  B.load(b1, BK);
-  A.store(a0, lds);
-  B.store(b0, lds + kOperandBytes);
+  O ld = mk(0);       // operands of the next slice to load,
+  int lt = 0, lk = 0;  // its tile and K slice
+  auto advance = [&]() {
+    if (++lk == ktiles && lt + 1 < count) {
+      lk = 0;
+      ld = mk(++lt);
+    }
+  };
+  ld.a.load(a0, 0);
+  ld.b.load(b0, 0);
+  advance();
+  ld.a.load(a1, lk * BK);
+  ld.b.load(b1, lk * BK);
+  advance();
+  ld.a.store(a0, lds);
+  ld.b.store(b0, lds + kOperandBytes);
   __syncthreads();
   read_frags<TA, TB>(fa0, fb0, lds, a_off, b_off, 0);
   char* s0 = lds;
   char* s1 = lds + kStageBytes;
-  int kt = 0;
-  for (; kt + 1 < ktiles; kt += 2) {
-    gemm_slice<T>(acc, s0, s1, A, B, a1, b1, a0, b0, fa0, fb0, fa1, fb1, a_off, b_off, (kt + 2) * BK);
-    gemm_slice<T>(acc, s1, s0, A, B, a0, b0, a1, b1, fa0, fb0, fa1, fb1, a_off, b_off, (kt + 3) * BK);
+  int ct = 0, ck = 0;  // tile and K slice being multiplied
+  const int total = count * ktiles;
+  for (int g = 0; g < total; g += 2) {
+    gemm_slice<T>(acc, s0, s1, ld.a, ld.b, a1, b1, a0, b0, fa0, fb0, fa1, fb1, a_off, b_off, lk * BK);
+    advance();
+    gemm_slice<T>(acc, s1, s0, ld.a, ld.b, a0, b0, a1, b1, fa0, fb0, fa1, fb1, a_off, b_off, lk * BK);
+    advance();
+    ck += 2;
+    if (ck == ktiles) {
+      epi(ct++, acc);
+      zero_acc(acc);
+      ck = 0;
+    }
   }
-  if (kt < ktiles) gemm_slice<T>(acc, s0, s1, A, B, a1, b1, a0, b0, fa0, fb0, fa1, fb1, a_off, b_off, (kt + 2) * BK);
   __builtin_amdgcn_s_setprio(0);
-  __syncthreads();  // the epilogue may reuse LDS
+}
+
+// Tiles of a 2-D grid handed out round-robin to `grid` persistent workgroups.
+__device__ __forceinline__ int my_tile_count(int tiles) {
+  return (tiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+}
+__device__ __forceinline__ int my_tile(int i) { return (int)blockIdx.x + i * (int)gridDim.x; }
+
+// K slices of a contraction of length K, rounded up to an even count for gemm_run.
+template <typename T> __device__ __forceinline__ int even_slices(int K) {
+  const int k = (K + kStageK<T> - 1) / kStageK<T>;
+  return k + (k & 1);
 }
 
 // ---------------------------------------------------------------------------------
 // Forward
 // ---------------------------------------------------------------------------------
 
-// Grid: one workgroup per (token tile, vocabulary tile), token tile fastest so the
-// workgroups resident at one time share a few W tiles.
+// LDS past the two GEMM stages, for the cross-wave (max, sum-exp) merge.
+constexpr int kRedBytes = 2 * kTile * (int)sizeof(float2);
+
+// Forward tiles.  Workgroup (nt, sp) = (blockIdx % n_tiles_n, blockIdx / n_tiles_n) owns
+// token tile nt and the vocabulary tiles sp, sp + splits, sp + 2 splits, ...; it keeps each
+// token's running (max, sum-exp) across those tiles (thread t < 256 holds token 256 nt + t)
+// and writes one partial per token to part[sp][n].  The label logit of a valid row is
+// written by the one lane whose tile holds the label.
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void fwd_tiles(const T* __restrict__ H, const T* __restrict__ W,
                                                           const int64_t* __restrict__ y, int N, int D, int V,
-                                                          int n_tiles_n, float2* __restrict__ part,
+                                                          int n_tiles_n, int splits, float2* __restrict__ part,
                                                           float* __restrict__ zlab) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
-  const int nt = blockIdx.x % n_tiles_n, vt = blockIdx.x / n_tiles_n;
-  const int v0 = vt * kTile, n0 = nt * kTile;
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes + kRedBytes];
+  const int nt = blockIdx.x % n_tiles_n, sp = blockIdx.x / n_tiles_n;
+  const int n_vt = (V + kTile - 1) / kTile;
+  const int count = (n_vt - sp + splits - 1) / splits;
+  const int n0 = nt * kTile;
   constexpr int BK = kStageK<T>;
-  f32x16 acc[kBM][kBN];
   const int ldb = D * (int)sizeof(T);
-  gemm_tile<T>(acc, lds, KTile<T>(W + (int64_t)v0 * D, ldb, V - v0, D), KTile<T>(H + (int64_t)n0 * D, ldb, N - n0, D),
-               (D + BK - 1) / BK);
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, t = threadIdx.x;
   const int wm = wave >> 2, wn = wave & 3, lr = lane & 31, lh = lane >> 5;
-  const int vbase = v0 + wm * kWaveM + 4 * lh;  // vocab row of acc[0][j][0] in this lane
-  const int vlim = V - vbase;                   // offsets below vlim are real rows
-  float mrow[kBN], srow[kBN];
+  float2* red = reinterpret_cast<float2*>(lds + kLdsBytes);  // [wm][token in tile]
+  int64_t lab[kBN];
 #pragma unroll
   for (int j = 0; j < kBN; ++j) {
     const int n = n0 + wn * kWaveN + 32 * j + lr;
-    const int64_t lab = n < N ? y[n] : -1;
-    const int64_t rel = lab - vbase;
-    float m = -__builtin_inff(), zl = 0.f;
-    bool hit = false;
+    lab[j] = n < N ? y[n] : -1;
+  }
+  float m_run = -__builtin_inff(), s_run = 0.f;
+
+  auto mk = [&](int i) {
+    const int v0 = (sp + i * splits) * kTile;
+    return Ops<KTile<T>, KTile<T>>{KTile<T>(W + (int64_t)v0 * D, ldb, V - v0, D),
+                                   KTile<T>(H + (int64_t)n0 * D, ldb, N - n0, D)};
+  };
+  auto epi = [&](int i, const f32x16 (&acc)[kBM][kBN]) {
+    const int v0 = (sp + i * splits) * kTile;
+    const int vbase = v0 + wm * kWaveM + 4 * lh;  // vocab row of acc[0][j][0] in this lane
+    const int vlim = V - vbase;                   // offsets below vlim are real rows
+    float mrow[kBN], srow[kBN];
 #pragma unroll
-    for (int i = 0; i < kBM; ++i)
+    for (int j = 0; j < kBN; ++j) {
+      const int n = n0 + wn * kWaveN + 32 * j + lr;
+      const int64_t rel = lab[j] - vbase;
+      float m = -__builtin_inff(), zl = 0.f;
+      bool hit = false;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int off = 32 * i + 8 * (r >> 2) + (r & 3);
-        const float z = acc[i][j][r];
-        if (off < vlim) m = fmaxf(m, z);
-        if (rel == off) {
-          zl = z;
-          hit = true;
-        }
-      }
-    float s = 0.f;
-    if (m != -__builtin_inff()) {
-      const float mb = m * kLog2e;
-#pragma unroll
-      for (int i = 0; i < kBM; ++i)
+      for (int ii = 0; ii < kBM; ++ii)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int off = 32 * i + 8 * (r >> 2) + (r & 3);
-          if (off < vlim) s += hw_exp2(__builtin_fmaf(acc[i][j][r], kLog2e, -mb));
+          const int off = 32 * ii + 8 * (r >> 2) + (r & 3);
+          const float z = acc[ii][j][r];
+          if (off < vlim) m = fmaxf(m, z);
+          if (rel == off) {
+            zl = z;
+            hit = true;
+          }
         }
-    }
-    lse_merge(m, s, __shfl_xor(m, 32), __shfl_xor(s, 32));
-    if (hit && n < N) zlab[n] = zl;
-    mrow[j] = m;
-    srow[j] = s;
-  }
-  __syncthreads();
-  float2* red = reinterpret_cast<float2*>(lds);  // [wm][token in tile]
-  if (lh == 0) {
+      float sum = 0.f;
+      if (m != -__builtin_inff()) {
+        const float mb = m * kLog2e;
 #pragma unroll
-    for (int j = 0; j < kBN; ++j) red[wm * kTile + wn * kWaveN + 32 * j + lr] = make_float2(mrow[j], srow[j]);
-  }
-  __syncthreads();
-  const int t = threadIdx.x;
-  if (t < kTile && n0 + t < N) {
-    float m = red[t].x, s = red[t].y;
-    lse_merge(m, s, red[kTile + t].x, red[kTile + t].y);
-    part[(int64_t)vt * N + n0 + t] = make_float2(m, s);
-  }
+        for (int ii = 0; ii < kBM; ++ii)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int off = 32 * ii + 8 * (r >> 2) + (r & 3);
+            if (off < vlim) sum += hw_exp2(__builtin_fmaf(acc[ii][j][r], kLog2e, -mb));
+          }
+      }
+      lse_merge(m, sum, __shfl_xor(m, 32), __shfl_xor(sum, 32));
+      if (hit && n < N) zlab[n] = zl;
+      mrow[j] = m;
+      srow[j] = sum;
+    }
+    if (lh == 0) {
+#pragma unroll
+      for (int j = 0; j < kBN; ++j) red[wm * kTile + wn * kWaveN + 32 * j + lr] = make_float2(mrow[j], srow[j]);
+    }
+    __syncthreads();
+    if (t < kTile) {
+      lse_merge(m_run, s_run, red[t].x, red[t].y);
+      lse_merge(m_run, s_run, red[kTile + t].x, red[kTile + t].y);
+    }
+  };
+  gemm_run<T>(lds, count, even_slices<T>(D), mk, epi);
+  if (t < kTile && n0 + t < N) part[(int64_t)sp * N + n0 + t] = make_float2(m_run, s_run);
 }
 
-__global__ __launch_bounds__(256) void fwd_combine(const float2* __restrict__ part, int n_vt,
+__global__ __launch_bounds__(256) void fwd_combine(const float2* __restrict__ part, int n_part,
                                                    const float* __restrict__ zlab, const int64_t* __restrict__ y,
                                                    int N, int V, int64_t ignore_index, float* __restrict__ lse,
                                                    double* __restrict__ blk_loss, int* __restrict__ blk_cnt,
@@ -474,8 +539,8 @@ __global__ __launch_bounds__(256) void fwd_combine(const float2* __restrict__ pa
   int c = 0, b = 0;
   if (n < N) {
     float m = -__builtin_inff(), s = 0.f;
-    for (int vt = 0; vt < n_vt; ++vt) {
-      const float2 p = part[(int64_t)vt * N + n];
+    for (int k = 0; k < n_part; ++k) {
+      const float2 p = part[(int64_t)k * N + n];
       lse_merge(m, s, p.x, p.y);
     }
     const float L = m + hw_log2(s) * kLn2;
@@ -570,7 +635,8 @@ template <> __device__ __forceinline__ void store4<float>(float* p, const float 
   *reinterpret_cast<float4*>(p) = make_float4(d[0], d[1], d[2], d[3]);
 }
 
-// dz tile of one (vocab chunk, token chunk); slab is [token in chunk][vocab in chunk].
+// dz tiles of one (vocab chunk, token chunk); slab is [token in chunk][vocab in chunk].
+// Persistent: tile b = (vt, tt) = (b / n_tiles_t, b % n_tiles_t), handed out round-robin.
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dz(const T* __restrict__ H, const T* __restrict__ W, int D,
                                                        int v0c, int vc_act, int t0c, int tc_act, int n_tiles_t,
@@ -578,46 +644,52 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dz(const T* __restrict__ H, c
                                                        const int* __restrict__ lab, T* __restrict__ slab,
                                                        int ld_slab) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
-  const int tt = blockIdx.x % n_tiles_t, vt = blockIdx.x / n_tiles_t;
-  const int vl0 = vt * kTile, tl0 = tt * kTile;
   constexpr int BK = kStageK<T>;
-  f32x16 acc[kBM][kBN];
   const int ldb = D * (int)sizeof(T);
-  gemm_tile<T>(acc, lds, KTile<T>(W + (int64_t)(v0c + vl0) * D, ldb, vc_act - vl0, D),
-               KTile<T>(H + (int64_t)(t0c + tl0) * D, ldb, tc_act - tl0, D), (D + BK - 1) / BK);
-
+  const int tiles = ((vc_act + kTile - 1) / kTile) * n_tiles_t;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 2, wn = wave & 3, lr = lane & 31, lh = lane >> 5;
-  const int vb = vl0 + wm * kWaveM + 4 * lh;  // chunk-local vocab row of acc[0][j][0]
-  const int vlim = vc_act - vb;
+  auto mk = [&](int i) {
+    const int b = my_tile(i);
+    const int vl0 = (b / n_tiles_t) * kTile, tl0 = (b % n_tiles_t) * kTile;
+    return Ops<KTile<T>, KTile<T>>{KTile<T>(W + (int64_t)(v0c + vl0) * D, ldb, vc_act - vl0, D),
+                                   KTile<T>(H + (int64_t)(t0c + tl0) * D, ldb, tc_act - tl0, D)};
+  };
+  auto epi = [&](int i, const f32x16 (&acc)[kBM][kBN]) {
+    const int b = my_tile(i);
+    const int vl0 = (b / n_tiles_t) * kTile, tl0 = (b % n_tiles_t) * kTile;
+    const int vb = vl0 + wm * kWaveM + 4 * lh;  // chunk-local vocab row of acc[0][j][0]
+    const int vlim = vc_act - vb;
 #pragma unroll
-  for (int j = 0; j < kBN; ++j) {
-    const int nl = tl0 + wn * kWaveN + 32 * j + lr;
-    float L2 = 0.f, cf = 0.f;
-    int rel = -1;
-    if (nl < tc_act) {
-      const int n = t0c + nl;
-      L2 = lse2[n];
-      cf = coef[n];
-      const int lb = lab[n];
-      rel = lb < 0 ? -1 : lb - v0c - vb;
-    }
-    T* out = slab + (int64_t)nl * ld_slab + vb;
-#pragma unroll
-    for (int i = 0; i < kBM; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float d[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int off = 32 * i + 8 * q + e;
-          float p = hw_exp2(__builtin_fmaf(acc[i][j][4 * q + e], kLog2e, -L2));
-          if (off == rel) p -= 1.f;
-          d[e] = off < vlim ? p * cf : 0.f;
-        }
-        store4<T>(out + 32 * i + 8 * q, d);
+    for (int j = 0; j < kBN; ++j) {
+      const int nl = tl0 + wn * kWaveN + 32 * j + lr;
+      float L2 = 0.f, cf = 0.f;
+      int rel = -1;
+      if (nl < tc_act) {
+        const int n = t0c + nl;
+        L2 = lse2[n];
+        cf = coef[n];
+        const int lb = lab[n];
+        rel = lb < 0 ? -1 : lb - v0c - vb;
       }
-  }
+      T* out = slab + (int64_t)nl * ld_slab + vb;
+#pragma unroll
+      for (int ii = 0; ii < kBM; ++ii)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float d[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int off = 32 * ii + 8 * q + e;
+            float p = hw_exp2(__builtin_fmaf(acc[ii][j][4 * q + e], kLog2e, -L2));
+            if (off == rel) p -= 1.f;
+            d[e] = off < vlim ? p * cf : 0.f;
+          }
+          store4<T>(out + 32 * ii + 8 * q, d);
+        }
+    }
+  };
+  gemm_run<T>(lds, my_tile_count(tiles), even_slices<T>(D), mk, epi);
 }
 
 template <typename TO> __device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, u32 off, float v);
@@ -676,44 +748,59 @@ __device__ __forceinline__ void tile_out(const f32x16 (&acc)[kBM][kBN], const fl
   }
 }
 
-// dH rows of one token chunk += slab x W[vocab chunk]; C[n][d].
-template <typename T>
+// dH rows of one token chunk (+)= slab x W[vocab chunk]; C[n][d].  Persistent over tiles
+// b = (mt, dt) = (b / n_tiles_d, b % n_tiles_d).  ACCUM: add the fp32 partial in dacc;
+// FINAL: write the sum to dH in the output type instead of back to dacc.
+template <typename T, bool ACCUM, bool FINAL>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dh(const T* __restrict__ slab, int ld_slab,
                                                        const T* __restrict__ W, int D, int v0c, int vc_act,
                                                        int t0c, int tc_act, int n_tiles_d,
-                                                       float* __restrict__ dacc, T* __restrict__ dH, int mode) {
+                                                       float* __restrict__ dacc, T* __restrict__ dH) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
-  const int dt = blockIdx.x % n_tiles_d, mt = blockIdx.x / n_tiles_d;
-  const int nl0 = mt * kTile, d0 = dt * kTile;
-  constexpr int BK = kStageK<T>;
-  f32x16 acc[kBM][kBN];
   const int es = (int)sizeof(T);
-  gemm_tile<T>(acc, lds, KTile<T>(slab + (int64_t)nl0 * ld_slab, ld_slab * es, tc_act - nl0, vc_act),
-               MNTile<T>(W + (int64_t)v0c * D + d0, D * es, D - d0, vc_act), (vc_act + BK - 1) / BK);
-  float* acc_tile = dacc + (int64_t)nl0 * D + d0;
-  const float* prev = (mode & kAccumulate) ? acc_tile : nullptr;
-  if (mode & kFinal)
-    tile_out<T>(acc, prev, dH + (int64_t)(t0c + nl0) * D + d0, D, tc_act - nl0, D - d0);
-  else
-    tile_out<float>(acc, prev, acc_tile, D, tc_act - nl0, D - d0);
+  const int tiles = ((tc_act + kTile - 1) / kTile) * n_tiles_d;
+  auto mk = [&](int i) {
+    const int b = my_tile(i);
+    const int nl0 = (b / n_tiles_d) * kTile, d0 = (b % n_tiles_d) * kTile;
+    return Ops<KTile<T>, MNTile<T>>{KTile<T>(slab + (int64_t)nl0 * ld_slab, ld_slab * es, tc_act - nl0, vc_act),
+                                    MNTile<T>(W + (int64_t)v0c * D + d0, D * es, D - d0, vc_act)};
+  };
+  auto epi = [&](int i, const f32x16 (&acc)[kBM][kBN]) {
+    const int b = my_tile(i);
+    const int nl0 = (b / n_tiles_d) * kTile, d0 = (b % n_tiles_d) * kTile;
+    float* acc_tile = dacc + (int64_t)nl0 * D + d0;
+    const float* prev = ACCUM ? acc_tile : nullptr;
+    if constexpr (FINAL)
+      tile_out<T>(acc, prev, dH + (int64_t)(t0c + nl0) * D + d0, D, tc_act - nl0, D - d0);
+    else
+      tile_out<float>(acc, prev, acc_tile, D, tc_act - nl0, D - d0);
+  };
+  gemm_run<T>(lds, my_tile_count(tiles), even_slices<T>(vc_act), mk, epi);
 }
 
-// dW rows of one vocab chunk (+)= slab^T x H[token chunk]; C[v][d].
-template <typename T>
+// dW rows of one vocab chunk (+)= slab^T x H[token chunk]; C[v][d].  Persistent over tiles
+// b = (mt, dt) = (b / n_tiles_d, b % n_tiles_d).
+template <typename T, bool ACCUM>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dw(const T* __restrict__ slab, int ld_slab,
                                                        const T* __restrict__ H, int D, int t0c, int tc_act,
-                                                       int v0c, int vc_act, int n_tiles_d,
-                                                       float* __restrict__ dW, int accumulate) {
+                                                       int v0c, int vc_act, int n_tiles_d, float* __restrict__ dW) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
-  const int dt = blockIdx.x % n_tiles_d, mt = blockIdx.x / n_tiles_d;
-  const int vl0 = mt * kTile, d0 = dt * kTile;
   constexpr int BK = kStageK<T>;
-  f32x16 acc[kBM][kBN];
   const int es = (int)sizeof(T);
-  gemm_tile<T>(acc, lds, MNTile<T>(slab + vl0, ld_slab * es, ld_slab - vl0, tc_act),
-               MNTile<T>(H + (int64_t)t0c * D + d0, D * es, D - d0, tc_act), (tc_act + BK - 1) / BK);
-  float* tile = dW + (int64_t)(v0c + vl0) * D + d0;
-  tile_out<float>(acc, accumulate ? tile : nullptr, tile, D, vc_act - vl0, D - d0);
+  const int tiles = ((vc_act + kTile - 1) / kTile) * n_tiles_d;
+  auto mk = [&](int i) {
+    const int b = my_tile(i);
+    const int vl0 = (b / n_tiles_d) * kTile, d0 = (b % n_tiles_d) * kTile;
+    return Ops<MNTile<T>, MNTile<T>>{MNTile<T>(slab + vl0, ld_slab * es, ld_slab - vl0, tc_act),
+                                     MNTile<T>(H + (int64_t)t0c * D + d0, D * es, D - d0, tc_act)};
+  };
+  auto epi = [&](int i, const f32x16 (&acc)[kBM][kBN]) {
+    const int b = my_tile(i);
+    const int vl0 = (b / n_tiles_d) * kTile, d0 = (b % n_tiles_d) * kTile;
+    float* tile = dW + (int64_t)(v0c + vl0) * D + d0;
+    tile_out<float>(acc, ACCUM ? tile : nullptr, tile, D, vc_act - vl0, D - d0);
+  };
+  gemm_run<T>(lds, my_tile_count(tiles), even_slices<T>(tc_act), mk, epi);
 }
 
 // ---------------------------------------------------------------------------------
@@ -737,18 +824,26 @@ bool sizes_ok(int64_t N, int64_t D, int64_t V, int dtype) {
 
 size_t elem_size(int dtype) { return dtype == FLCE_BF16 ? 2 : 4; }
 
+// Workgroups resident at once: one 512-thread, ~150 KB-LDS workgroup per CU, 256 CUs.
+constexpr int kPersistentWGs = 256;
+
 struct FwdLayout {
   size_t part, zlab, bloss, bcnt, bbad, total;
-  int n_vt, nblk;
+  int splits, nblk;
 };
 
+// Forward: ceil(N / 256) token tiles, each shared by `splits` workgroups that split the
+// vocabulary tiles between them (token tiles x splits ~ the resident workgroups).
 FwdLayout fwd_layout(int64_t N, int64_t V) {
   FwdLayout L;
-  L.n_vt = (int)ceil_div(V, kTile);
+  const int64_t ntn = ceil_div(N, kTile), n_vt = ceil_div(V, kTile);
+  int64_t sp = kPersistentWGs / ntn;
+  sp = sp < 1 ? 1 : (sp > n_vt ? n_vt : sp);
+  L.splits = (int)sp;
   L.nblk = (int)ceil_div(N, 256);
   size_t off = 0;
   L.part = off;
-  off += region((size_t)L.n_vt * (size_t)N * sizeof(float2));
+  off += region((size_t)L.splits * (size_t)N * sizeof(float2));
   L.zlab = off;
   off += region((size_t)N * sizeof(float));
   L.bloss = off;
@@ -837,8 +932,9 @@ flce_status forward_impl(const T* H, const T* W, const int64_t* y, int N, int D,
   int* bbad = reinterpret_cast<int*>(ws + L.bbad);
   const int ntn = (int)ceil_div(N, kTile);
   (void)hipGetLastError();
-  fwd_tiles<T><<<dim3((unsigned)ntn * (unsigned)L.n_vt), dim3(kThreads), 0, s>>>(H, W, y, N, D, V, ntn, part, zlab);
-  fwd_combine<<<dim3(L.nblk), dim3(256), 0, s>>>(part, L.n_vt, zlab, y, N, V, ignore_index, lse, bloss, bcnt, bbad);
+  fwd_tiles<T><<<dim3((unsigned)ntn * (unsigned)L.splits), dim3(kThreads), 0, s>>>(H, W, y, N, D, V, ntn, L.splits,
+                                                                                   part, zlab);
+  fwd_combine<<<dim3(L.nblk), dim3(256), 0, s>>>(part, L.splits, zlab, y, N, V, ignore_index, lse, bloss, bcnt, bbad);
   fwd_finalize<<<dim3(1), dim3(256), 0, s>>>(bloss, bcnt, bbad, L.nblk, loss, n_valid, dev_status);
   return launched();
 }
@@ -857,25 +953,39 @@ flce_status backward_impl(const T* H, const T* W, const int64_t* y, const float*
   (void)hipGetLastError();
   bwd_prep<<<dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, s>>>(lse, y, n_valid, grad, N, V, ignore_index, lse2,
                                                                   coef, lab);
+  // Chunks of whole 256-row tiles, spread evenly: chunk i of n covers tiles
+  // [i T / n, (i + 1) T / n) of the T tiles, never more than the workspace's chunk size.
   const int n_tc = (int)ceil_div(N, L.tc), n_vc = (int)ceil_div(V, L.vc);
+  const int64_t t_tiles = ceil_div(N, kTile), v_tiles = ceil_div(V, kTile);
+  auto grid = [](int tiles) { return (unsigned)(tiles < kPersistentWGs ? tiles : kPersistentWGs); };
   for (int ci = 0; ci < n_tc; ++ci) {
-    const int t0c = (int)(ci * L.tc);
-    const int tc_act = (int)((N - t0c) < L.tc ? (N - t0c) : L.tc);
+    const int t0c = (int)(ci * t_tiles / n_tc * kTile);
+    const int t1c = (int)((ci + 1) * t_tiles / n_tc * kTile);
+    const int tc_act = (t1c < N ? t1c : N) - t0c;
     const int n_tt = (int)ceil_div(tc_act, kTile);
     // fp32 accumulates dH in place; bf16 accumulates in the workspace and converts last.
     float* acc_rows = dacc ? dacc : reinterpret_cast<float*>(dH) + (int64_t)t0c * D;
     for (int vi = 0; vi < n_vc; ++vi) {
-      const int v0c = (int)(vi * L.vc);
-      const int vc_act = (int)((V - v0c) < L.vc ? (V - v0c) : L.vc);
+      const int v0c = (int)(vi * v_tiles / n_vc * kTile);
+      const int v1c = (int)((vi + 1) * v_tiles / n_vc * kTile);
+      const int vc_act = (v1c < V ? v1c : V) - v0c;
       const int n_vt = (int)ceil_div(vc_act, kTile);
-      bwd_dz<T><<<dim3((unsigned)(n_vt * n_tt)), dim3(kThreads), 0, s>>>(H, W, D, v0c, vc_act, t0c, tc_act, n_tt,
-                                                                        lse2, coef, lab, slab, ld_slab);
-      int mode = vi > 0 ? kAccumulate : 0;
-      if (dacc && vi == n_vc - 1) mode |= kFinal;
-      bwd_dh<T><<<dim3((unsigned)(n_tt * n_td)), dim3(kThreads), 0, s>>>(slab, ld_slab, W, D, v0c, vc_act, t0c,
-                                                                         tc_act, n_td, acc_rows, dH, mode);
-      bwd_dw<T><<<dim3((unsigned)(n_vt * n_td)), dim3(kThreads), 0, s>>>(slab, ld_slab, H, D, t0c, tc_act, v0c,
-                                                                         vc_act, n_td, dW, ci > 0 ? 1 : 0);
+      bwd_dz<T><<<dim3(grid(n_vt * n_tt)), dim3(kThreads), 0, s>>>(H, W, D, v0c, vc_act, t0c, tc_act, n_tt, lse2,
+                                                                   coef, lab, slab, ld_slab);
+      const dim3 gh(grid(n_tt * n_td)), gw(grid(n_vt * n_td)), blk(kThreads);
+      const bool acc_dh = vi > 0, fin = dacc && vi == n_vc - 1;
+      if (!acc_dh && !fin)
+        bwd_dh<T, false, false><<<gh, blk, 0, s>>>(slab, ld_slab, W, D, v0c, vc_act, t0c, tc_act, n_td, acc_rows, dH);
+      else if (acc_dh && !fin)
+        bwd_dh<T, true, false><<<gh, blk, 0, s>>>(slab, ld_slab, W, D, v0c, vc_act, t0c, tc_act, n_td, acc_rows, dH);
+      else if (!acc_dh && fin)
+        bwd_dh<T, false, true><<<gh, blk, 0, s>>>(slab, ld_slab, W, D, v0c, vc_act, t0c, tc_act, n_td, acc_rows, dH);
+      else
+        bwd_dh<T, true, true><<<gh, blk, 0, s>>>(slab, ld_slab, W, D, v0c, vc_act, t0c, tc_act, n_td, acc_rows, dH);
+      if (ci > 0)
+        bwd_dw<T, true><<<gw, blk, 0, s>>>(slab, ld_slab, H, D, t0c, tc_act, v0c, vc_act, n_td, dW);
+      else
+        bwd_dw<T, false><<<gw, blk, 0, s>>>(slab, ld_slab, H, D, t0c, tc_act, v0c, vc_act, n_td, dW);
     }
   }
   return launched();

@@ -44,8 +44,9 @@ def _r(x, a=256):
 
 
 def _fwd_bytes(N, V):
-    nvt, nblk = -(-V // 256), -(-N // 256)
-    return _r(nvt * N * 8) + _r(N * 4) + _r(nblk * 8) + 2 * _r(nblk * 4)
+    ntn, nvt = -(-N // 256), -(-V // 256)
+    splits = min(max(256 // ntn, 1), nvt)
+    return _r(splits * N * 8) + _r(N * 4) + _r(ntn * 8) + 2 * _r(ntn * 4)
 
 
 def _bwd_bytes(N, D, esize, tc, vc, bf16):
