@@ -7,24 +7,28 @@
 // dH and dW; the [N, V] logit and gradient tensors never reach HBM in full.
 //
 // Layout of the work on the chip:
-//   * One GEMM core for every contraction: a 256 x 256 output tile per 256-thread
-//     workgroup (four wave64s, each owning 128 x 128 as 4 x 4 MFMA blocks of 32 x 32),
-//     K staged through LDS in 128-byte slices, double buffered, one barrier per slice.
-//     bf16 uses v_mfma_f32_32x32x16_bf16; fp32 uses v_mfma_f32_32x32x2_f32.
-//   * LDS rows are K-contiguous with a 144-byte pitch (16 bytes of padding), so the
-//     ds_read_b128 fragment reads of 8 or 16 consecutive rows hit distinct banks.
+//   * One GEMM core for every contraction: a 256 x 256 output tile per 512-thread
+//     workgroup (eight wave64s, two per SIMD, each owning 128 x 64 as 4 x 2 MFMA blocks
+//     of 32 x 32), K staged through LDS in 128-byte slices, double buffered, one barrier
+//     per slice.  Workgroups are persistent: each walks a list of tiles with one
+//     continuous load pipeline.  bf16 uses v_mfma_f32_32x32x16_bf16; fp32 uses
+//     v_mfma_f32_32x32x2_f32.
+//   * Operands move HBM -> LDS with direct DMA loads (no register staging), into
+//     unpadded LDS rows whose 16-byte chunks are XOR-swizzled so fragment reads are free
+//     of bank conflicts.
 //   * Operands whose rows are K-contiguous in HBM (H and W for the logits, the dz slab
-//     for dH) are copied straight into LDS.  Operands contracted over their row index
-//     (W for dH; H and the slab for dW) are "MN-contiguous": each thread loads an 8 x 8
-//     (bf16) or 4 x 4 (fp32) block with 16-byte row-coalesced loads and transposes it in
-//     registers before the LDS store, so every contraction reads LDS the same way.
+//     for dH) are read from LDS with ds_read_b128.  Operands contracted over their row
+//     index (W for dH; H and the slab for dW) are "MN-contiguous": LDS keeps them as they
+//     are in HBM, and bf16 fragments come out transposed through ds_read_b64_tr_b16 (fp32
+//     ones as four ds_read_b32, the fp32 MFMA taking one K value per lane).
 //   * The logit tile is computed transposed, Z^T[v][n]: in the 32 x 32 MFMA result a
 //     lane holds one token column and 16 vocabulary rows, so the per-token max and
 //     sum-exp are in-lane reductions plus one exchange with lane ^ 32.
 //
 // Kernels:
-//   fwd_tiles     Z^T tile (W x H^T over D) -> per (vocab tile, token) (max, sum-exp)
-//                 partials and the label logit (compare in the epilogue).
+//   fwd_tiles     Z^T tiles (W x H^T over D); each workgroup keeps a running (max,
+//                 sum-exp) per token over the vocabulary tiles it owns -> one partial per
+//                 (workgroup, token), and the label logit (compare in the epilogue).
 //   fwd_combine   merge partials per token in fixed order -> lse, row loss; block sums.
 //   fwd_finalize  fixed-order sum of block sums -> loss, N_valid, dev_status.
 //   bwd_prep      per-row lse*log2(e), g/N_valid (0 for ignored rows), label.
@@ -55,11 +59,10 @@ constexpr int kThreads = 512;                      // eight wave64s, two per SIM
 constexpr int kTile = 256;                         // output tile edge
 constexpr int kWaveM = 128, kWaveN = 64;           // per-wave output block (2 x 4 waves)
 constexpr int kBM = kWaveM / 32, kBN = kWaveN / 32;  // 32 x 32 MFMA blocks per wave
-constexpr int kKBytes = 128;                       // K bytes per LDS row per stage
-constexpr int kLdsRow = 144;                       // LDS row pitch in bytes
-constexpr int kOperandBytes = kTile * kLdsRow;     // one operand, one stage
+constexpr int kKBytes = 128;                       // K bytes per tile element per stage
+constexpr int kOperandBytes = kTile * kKBytes;     // one operand, one stage: 32 KiB
 constexpr int kStageBytes = 2 * kOperandBytes;     // A and B
-constexpr int kLdsBytes = 2 * kStageBytes;         // two stages: 147456 of 163840
+constexpr int kLdsBytes = 2 * kStageBytes;         // two stages: 131072 of 163840
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -93,13 +96,21 @@ template <> __device__ __forceinline__ u16 from_f32<u16>(float f) { return (u16)
 template <> __device__ __forceinline__ float from_f32<float>(float f) { return f; }
 
 // ---------------------------------------------------------------------------------
-// Global -> LDS operand staging.  A tile operand covers kTile rows (r) by one K slice.
-// LDS row r, 16-byte chunk c holds K elements [c * kPerChunk, (c + 1) * kPerChunk).
-// Loads go through buffer descriptors: an offset at or past the descriptor's size reads
-// zeros, so ragged edges need no branches (out-of-range chunks use kOOB).
+// Global -> LDS operand staging.  A tile operand covers kTile tile elements by one K slice
+// of kKBytes bytes per element (32 KiB).  Loads are direct global -> LDS DMA loads
+// (buffer_load_dwordx4 ... lds): one wave-wide load moves lane i's 16 bytes to LDS byte
+// 16 i past a wave-uniform address, whatever global address the lane reads, so the LDS
+// layout is chosen by which global chunk each lane fetches.  Wave w fills LDS bytes
+// [4096 w, 4096 w + 4096) of each operand with four such loads.  Loads go through buffer
+// descriptors: an offset at or past the descriptor's size reads (and writes to LDS) zeros,
+// so ragged edges need no branches (masked chunks use the offset kOOB).
 // ---------------------------------------------------------------------------------
 
 constexpr u32 kOOB = 0x7ffffff0u;
+constexpr int kDmaBytes = 1024;                                 // one wave-wide DMA load
+constexpr int kDmaPerWave = kOperandBytes / kDmaBytes / (kThreads / 64);  // 4
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 // Descriptor fields are workgroup-uniform; readfirstlane lets the compiler keep the
 // descriptor in SGPRs instead of looping over lanes around every load.
@@ -111,135 +122,175 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, u3
   return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
-__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, u32 off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+// Raw descriptor words (the fields make_rsrc sets) for the DMA loads below.
+__device__ __forceinline__ u32x4 dma_rsrc(const void* base, u32 bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{(u32)__builtin_amdgcn_readfirstlane((u32)a),
+               (u32)__builtin_amdgcn_readfirstlane((u32)(a >> 32)) & 0xffffu,
+               (u32)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
 }
 
-// Rows K-contiguous in HBM: tile row r (0..255) starts at base + r * ld_bytes; rows at or
-// beyond rows_ok fall outside the descriptor; K elements at or beyond k_lim are masked
+// This wave's four DMA loads of one operand stage: lane offsets v[i] (kOOB for zeros).
+// Issued as inline assembly: the compiler's wait-count pass, which cannot tell the LDS
+// bytes a DMA load writes from the ones a ds_read_b64_tr_b16 reads, would otherwise wait
+// for every outstanding DMA load before each transposing read.  The wait that matters is
+// explicit: dma_barrier drains this wave's loads before the workgroup barrier that hands
+// the stage to the other waves.  M0 (the DMA's LDS base) is set here and used by nothing
+// else in these kernels; the loads retire in order with the compiler's own loads, so the
+// compiler's counts for those stay conservative.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_operand(const u32x4& r, char* op, const u32 (&v)[kDmaPerWave]) {
+  const u32 w = (u32)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const u32 base = (u32)reinterpret_cast<uintptr_t>((lds_void*)op) + w * (u32)(kDmaPerWave * kDmaBytes);
+#pragma unroll
+  for (int i = 0; i < kDmaPerWave; ++i)
+    asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds" ::"v"(v[i]),
+                 "s"(base + (u32)(i * kDmaBytes)), "s"(r)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Fragment addresses: one per K step (KTile) or per 32-element block (MNTile), at most 4.
+typedef int FragAddr[4];
+
+// Rows K-contiguous in HBM: tile element r's K row starts at base + r * ld_bytes; rows at
+// or beyond rows_ok fall outside the descriptor; K elements at or beyond k_lim are masked
 // (k_lim a multiple of kPerChunk, or the data past it zero, as in the dz slab).
-// Thread t moves 16-byte chunk t & 7 of rows (t >> 3) + 64 i, i = 0..3.
+// LDS: row r (0..255) holds its kKBytes of K as eight 16-byte chunks, chunk c in slot
+// c ^ ((r >> 1) & 7), so sixteen consecutive rows read at one chunk hit distinct banks.
+// DMA i of wave w fills rows 8 (4 w + i) .. +7: lane L takes row + (L >> 3), slot L & 7.
 template <typename T> struct KTile {
   static constexpr int kFragReads = 1;
-  // byte offset, within the operand, of this lane's fragment for tile elements elem0 ..
-  static __device__ __forceinline__ int frag_base(int elem0, int lane) {
-    return (elem0 + (lane & 31)) * kLdsRow + (lane >> 5) * 16;
+  static __device__ __forceinline__ void frag_addrs(FragAddr& a, int elem0, int lane) {
+    const int row = elem0 + (lane & 31), sw = (lane >> 1) & 7, h = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) a[ks] = row * kKBytes + 16 * ((2 * ks + h) ^ sw);
   }
-  // fragment of the 32-element block blk (from elem0) and K step ks
-  static __device__ __forceinline__ u32x4 frag(const char* op, int base, int blk, int ks) {
-    return *reinterpret_cast<const u32x4*>(op + base + blk * 32 * kLdsRow + ks * 32);
+  // 16-byte fragment of the 32-element block blk and K step ks: 8 bf16 or 4 fp32 K values
+  static __device__ __forceinline__ u32x4 frag(const char* op, const FragAddr& a, int blk, int ks) {
+    return *reinterpret_cast<const u32x4*>(op + a[ks] + blk * 32 * kKBytes);
   }
-  __amdgpu_buffer_rsrc_t rsrc;
-  u32 voff, rstep;
-  int kc, k_lim;
+  u32x4 rsrc;
+  u32 voff[kDmaPerWave];
+  int kc[kDmaPerWave];  // first K element of each lane's chunk
+  int k_lim;
   __device__ __forceinline__ KTile(const T* base, int ld_bytes, int rows_ok, int k_lim_) {
-    const int t = threadIdx.x;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int rows = rows_ok < 0 ? 0 : (rows_ok > kTile ? kTile : rows_ok);
-    rsrc = make_rsrc(base, (u32)rows * (u32)ld_bytes);
-    kc = (t & 7) * Elem<T>::kPerChunk;
+    rsrc = dma_rsrc(base, (u32)rows * (u32)ld_bytes);
     k_lim = k_lim_;
-    voff = (u32)(t >> 3) * (u32)ld_bytes + (u32)kc * sizeof(T);
-    rstep = 64u * (u32)ld_bytes;
-  }
-  __device__ __forceinline__ void load(u32x4 (&reg)[4], int k0) const {
-    const bool kok = k0 + kc < k_lim;
-    const u32 o = voff + (u32)k0 * sizeof(T);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) reg[i] = bload(rsrc, kok ? o + (u32)i * rstep : kOOB);
+    for (int i = 0; i < kDmaPerWave; ++i) {
+      const int r = 8 * (kDmaPerWave * w + i) + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      kc[i] = c * Elem<T>::kPerChunk;
+      voff[i] = (u32)r * (u32)ld_bytes + (u32)c * 16u;
+    }
   }
-  __device__ __forceinline__ void store(const u32x4 (&reg)[4], char* lds) const {
-    const int t = threadIdx.x;
+  __device__ __forceinline__ void load(char* op, int k0) const {
+    u32 v[kDmaPerWave];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4*>(lds + (i * 64 + (t >> 3)) * kLdsRow + (t & 7) * 16) = reg[i];
+    for (int i = 0; i < kDmaPerWave; ++i) v[i] = k0 + kc[i] < k_lim ? voff[i] + (u32)k0 * (u32)sizeof(T) : kOOB;
+    dma_operand(rsrc, op, v);
   }
 };
 
-// Rows MN-contiguous in HBM: element (tile row c, k) at base + k * ld_bytes + c * sizeof(T)
-// where base is the tile's first column; K rows at or beyond k_lim fall outside the
-// descriptor, tile rows at or beyond cols_ok (a multiple of kPerChunk) are masked.  fp32
-// tiles are transposed in registers before the LDS store; bf16 tiles are stored as they
-// are and transposed by the LDS read.
+// Rows MN-contiguous in HBM: element (tile element e, k) at base + k * ld_bytes + e * sizeof(T)
+// where base is the tile's first element; K rows at or beyond k_lim fall outside the
+// descriptor, tile elements at or beyond cols_ok (a multiple of kPerChunk) are masked.
 template <typename T> struct MNTile;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-// bf16: the K slice is copied into LDS untransposed, as 64 rows k of 256 tile elements
-// (row pitch kTrPitch), and transposed on the way out by ds_read_b64_tr_b16.  Within each
-// 16-lane group that instruction hands lane i the elements i, 16 + i, 32 + i, 48 + i of the
-// group's sixteen 4-element loads; a lane j addressing row k0 + (j >> 2), elements
-// n0 + 4 (j & 3) .. + 3 therefore delivers column n0 + i at rows k0 .. k0 + 3 to lane i, half
-// of a 32 x 32 x 16 MFMA fragment.
-constexpr int kTrPitch = 576;  // 512 bytes of row + 64: four consecutive rows cover 256 bytes of banks
-
+// bf16: LDS holds the slice as it is in HBM, 64 K rows of 256 elements (512 bytes, 32
+// chunks; chunk c in slot c ^ (4 (k & 3))), and ds_read_b64_tr_b16 transposes on the way
+// out.  Within each 16-lane group that instruction hands lane i the elements i, 16 + i,
+// 32 + i, 48 + i of the group's sixteen 4-element loads; a lane j addressing row
+// k0 + (j >> 2), elements n0 + 4 (j & 3) .. + 3 therefore delivers element n0 + i at rows
+// k0 .. k0 + 3 to lane i, half of a 32 x 32 x 16 MFMA fragment.  The 32 lanes of a half-wave
+// read four rows of 64 bytes, which the swizzle spreads over all banks.
+// DMA i of wave w fills K rows 2 (4 w + i) and + 1: lane L takes row + (L >> 5), slot L & 31.
 template <> struct MNTile<u16> {
   static constexpr int kFragReads = 2;
-  // thread t moves 16-byte chunk t & 31 (tile elements 8 (t & 31) .. +7) of K rows (t >> 5) + 16 i
-  __amdgpu_buffer_rsrc_t rsrc;
-  u32 voff, ld;
-  bool cok;
-  __device__ __forceinline__ MNTile(const u16* base, int ld_bytes, int cols_ok, int k_lim) {
-    const int t = threadIdx.x;
-    rsrc = make_rsrc(base, k_lim < 0 ? 0u : (u32)k_lim * (u32)ld_bytes);
-    cok = (t & 31) * 8 < cols_ok;
-    ld = (u32)ld_bytes;
-    voff = (u32)(t >> 5) * ld + (u32)(t & 31) * 16u;
-  }
-  __device__ __forceinline__ void load(u32x4 (&reg)[4], int k0) const {
-    const u32 o = voff + (u32)k0 * ld;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) reg[i] = bload(rsrc, cok ? o + (u32)(16 * i) * ld : kOOB);
-  }
-  __device__ __forceinline__ void store(const u32x4 (&reg)[4], char* lds) const {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4*>(lds + ((t >> 5) + 16 * i) * kTrPitch + (t & 31) * 16) = reg[i];
-  }
-  static __device__ __forceinline__ int frag_base(int elem0, int lane) {
+  static constexpr int kRow = kTile * 2;
+  static __device__ __forceinline__ void frag_addrs(FragAddr& a, int elem0, int lane) {
     const int g = lane >> 4, j = lane & 15;
-    return (8 * (g >> 1) + (j >> 2)) * kTrPitch + (elem0 + 16 * (g & 1) + 4 * (j & 3)) * 2;
+    const int k = 8 * (g >> 1) + (j >> 2);
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      const int e = elem0 + 32 * blk + 16 * (g & 1) + 4 * (j & 3);
+      a[blk] = k * kRow + ((e >> 3) ^ (4 * (k & 3))) * 16 + (e & 7) * 2;
+    }
   }
-  static __device__ __forceinline__ u32x4 frag(const char* op, int base, int blk, int ks) {
-    char* p = const_cast<char*>(op) + base + blk * 64 + ks * 16 * kTrPitch;
+  static __device__ __forceinline__ u32x4 frag(const char* op, const FragAddr& a, int blk, int ks) {
+    char* p = const_cast<char*>(op) + a[blk] + ks * 16 * kRow;
     const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
-    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 4 * kTrPitch));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 4 * kRow));
     const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
     return u32x4{l2[0], l2[1], h2[0], h2[1]};
   }
+  u32x4 rsrc;
+  u32 voff[kDmaPerWave], ld;
+  __device__ __forceinline__ MNTile(const u16* base, int ld_bytes, int cols_ok, int k_lim) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    rsrc = dma_rsrc(base, k_lim < 0 ? 0u : (u32)k_lim * (u32)ld_bytes);
+    ld = (u32)ld_bytes;
+#pragma unroll
+    for (int i = 0; i < kDmaPerWave; ++i) {
+      const int k = 2 * (kDmaPerWave * w + i) + (lane >> 5);
+      const int c = (lane & 31) ^ (4 * (k & 3));
+      voff[i] = c * 8 < cols_ok ? (u32)k * ld + (u32)c * 16u : kOOB;
+    }
+  }
+  __device__ __forceinline__ void load(char* op, int k0) const {
+    u32 v[kDmaPerWave];
+#pragma unroll
+    for (int i = 0; i < kDmaPerWave; ++i) v[i] = voff[i] == kOOB ? kOOB : voff[i] + (u32)k0 * ld;
+    dma_operand(rsrc, op, v);
+  }
 };
 
+// fp32: LDS holds 32 K rows of 256 floats (1024 bytes, 64 chunks; chunk c in slot
+// c ^ (8 ((k >> 2) & 1))).  The fp32 MFMA takes one K value per lane, so a fragment is four
+// ds_read_b32 of rows 8 ks + 4 (l >> 5) + e, e = 0..3, at the lane's element: the same K
+// order as the KTile chunks.  The two half-waves read rows four apart, which the swizzle
+// puts 128 bytes apart in the banks.  DMA i of wave w fills K row 4 w + i.
 template <> struct MNTile<float> {
-  // thread t moves the 4 x 4 block of tile rows 4 (t >> 3) .. +3 and K elements 4 (t & 7) .. +3,
-  // transposed, into the K-contiguous layout KTile uses
-  static constexpr int kFragReads = 1;
-  static __device__ __forceinline__ int frag_base(int elem0, int lane) { return KTile<float>::frag_base(elem0, lane); }
-  static __device__ __forceinline__ u32x4 frag(const char* op, int base, int blk, int ks) {
-    return KTile<float>::frag(op, base, blk, ks);
-  }
-  __amdgpu_buffer_rsrc_t rsrc;
-  u32 voff, ld;
-  bool cok;
-  __device__ __forceinline__ MNTile(const float* base, int ld_bytes, int cols_ok, int k_lim) {
-    const int t = threadIdx.x;
-    rsrc = make_rsrc(base, k_lim < 0 ? 0u : (u32)k_lim * (u32)ld_bytes);
-    ld = (u32)ld_bytes;
-    cok = (t >> 3) * 4 < cols_ok;
-    voff = (u32)((t & 7) * 4) * ld + (u32)((t >> 3) * 4) * 4u;
-  }
-  __device__ __forceinline__ void load(u32x4 (&reg)[4], int k0) const {
-    const u32 o = voff + (u32)k0 * ld;
+  static constexpr int kFragReads = 4;
+  static constexpr int kRow = kTile * 4;
+  static __device__ __forceinline__ void frag_addrs(FragAddr& a, int elem0, int lane) {
+    const int h = lane >> 5;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) reg[i] = bload(rsrc, cok ? o + (u32)i * ld : kOOB);
-  }
-  __device__ __forceinline__ void store(const u32x4 (&reg)[4], char* lds) const {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const u32x4 o = {reg[0][e], reg[1][e], reg[2][e], reg[3][e]};
-      *reinterpret_cast<u32x4*>(lds + ((t >> 3) * 4 + e) * kLdsRow + (t & 7) * 16) = o;
+    for (int blk = 0; blk < 4; ++blk) {
+      const int e = elem0 + 32 * blk + (lane & 31);
+      a[blk] = 4 * h * kRow + ((e >> 2) ^ (8 * h)) * 16 + (e & 3) * 4;
     }
+  }
+  static __device__ __forceinline__ u32x4 frag(const char* op, const FragAddr& a, int blk, int ks) {
+    const char* p = op + a[blk] + 8 * ks * kRow;
+    return u32x4{*reinterpret_cast<const u32*>(p), *reinterpret_cast<const u32*>(p + kRow),
+                 *reinterpret_cast<const u32*>(p + 2 * kRow), *reinterpret_cast<const u32*>(p + 3 * kRow)};
+  }
+  u32x4 rsrc;
+  u32 voff[kDmaPerWave], ld;
+  __device__ __forceinline__ MNTile(const float* base, int ld_bytes, int cols_ok, int k_lim) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    rsrc = dma_rsrc(base, k_lim < 0 ? 0u : (u32)k_lim * (u32)ld_bytes);
+    ld = (u32)ld_bytes;
+#pragma unroll
+    for (int i = 0; i < kDmaPerWave; ++i) {
+      const int k = kDmaPerWave * w + i;
+      const int c = lane ^ (8 * ((k >> 2) & 1));
+      voff[i] = c * 4 < cols_ok ? (u32)k * ld + (u32)c * 16u : kOOB;
+    }
+  }
+  __device__ __forceinline__ void load(char* op, int k0) const {
+    u32 v[kDmaPerWave];
+#pragma unroll
+    for (int i = 0; i < kDmaPerWave; ++i) v[i] = voff[i] == kOOB ? kOOB : voff[i] + (u32)k0 * ld;
+    dma_operand(rsrc, op, v);
   }
 };
 
@@ -271,12 +322,12 @@ template <> struct Mfma<float> {
 };
 
 template <typename TA, typename TB>
-__device__ __forceinline__ void read_frags(u32x4 (&fa)[kBM], u32x4 (&fb)[kBN], const char* stage, int a_base,
-                                           int b_base, int ks) {
+__device__ __forceinline__ void read_frags(u32x4 (&fa)[kBM], u32x4 (&fb)[kBN], const char* stage, const FragAddr& aa,
+                                           const FragAddr& ab, int ks) {
 #pragma unroll
-  for (int i = 0; i < kBM; ++i) fa[i] = TA::frag(stage, a_base, i, ks);
+  for (int i = 0; i < kBM; ++i) fa[i] = TA::frag(stage, aa, i, ks);
 #pragma unroll
-  for (int j = 0; j < kBN; ++j) fb[j] = TB::frag(stage + kOperandBytes, b_base, j, ks);
+  for (int j = 0; j < kBN; ++j) fb[j] = TB::frag(stage + kOperandBytes, ab, j, ks);
 }
 
 template <typename T>
@@ -307,42 +358,45 @@ __device__ __forceinline__ void sched_step() {
   }
 }
 
-typedef u32x4 Stage4[4];  // one thread's share of one operand's K slice
+// Wait for this wave's outstanding global -> LDS loads (vmcnt 0; expcnt and lgkmcnt left
+// at their maxima), then synchronise the workgroup.
+__device__ __forceinline__ void dma_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+  __syncthreads();
+}
 
-// One K slice (four 16-element K steps).  On entry the fragments of step 0 of `cur` are in
-// fa0/fb0 and the registers sa/sb hold slice kt + 1 (loaded one slice earlier).  The slice
-// stores sa/sb into `nxt`, starts loading slice kt + 2 into la/lb, runs steps 0-2 reading
-// each next step's fragments one step ahead, synchronises, reads step 0 of `nxt` and runs
-// step 3 on fragments already in registers, so the fragment latency after the barrier is
-// covered by MFMAs.  Loads of slices beyond K read zeros (the descriptors' ranges end).
-// Two waves share each SIMD; a wave raises its priority once past the barrier so the
-// matrix core keeps being fed while its partner finishes the previous slice.
+// One K slice (four 16-element K steps) on LDS stage `cur`.  On entry the fragments of
+// step 0 are in fa0/fb0 and the DMA loads of the next slice into `nxt` are in flight.
+// Steps 0-2 read each next step's fragments one step ahead; the barrier then waits for
+// the next slice's loads and for every wave's reads of `cur`, after which the loads of the
+// slice after next (k_load) go into `cur` once step 0 of `nxt` is read, and step 3 runs on
+// fragments already in registers, so the fragment latency after the barrier is covered
+// by MFMAs.  A load issued right after one barrier has a whole slice of MFMAs until the
+// next.  Two waves share each SIMD; a wave raises its priority once past the barrier so
+// the matrix core keeps being fed while its partner finishes the previous slice.
 template <typename T, typename TA, typename TB>
-__device__ __forceinline__ void gemm_slice(f32x16 (&acc)[kBM][kBN], const char* cur, char* nxt, const TA& A,
-                                           const TB& B, Stage4& sa, Stage4& sb, Stage4& la, Stage4& lb,
-                                           u32x4 (&fa0)[kBM], u32x4 (&fb0)[kBN], u32x4 (&fa1)[kBM],
-                                           u32x4 (&fb1)[kBN], int a_base, int b_base, int k_load) {
+__device__ __forceinline__ void gemm_slice(f32x16 (&acc)[kBM][kBN], char* cur, const char* nxt, const TA& A,
+                                           const TB& B, u32x4 (&fa0)[kBM], u32x4 (&fb0)[kBN], u32x4 (&fa1)[kBM],
+                                           u32x4 (&fb1)[kBN], const FragAddr& aa, const FragAddr& ab, int k_load) {
   constexpr int M = Mfma<T>::kPerFrag;
   constexpr int R = kBM * TA::kFragReads + kBN * TB::kFragReads;  // LDS reads per K step
-  A.store(sa, nxt);
-  B.store(sb, nxt + kOperandBytes);
-  A.load(la, k_load);
-  B.load(lb, k_load);
-  read_frags<TA, TB>(fa1, fb1, cur, a_base, b_base, 1);
+  read_frags<TA, TB>(fa1, fb1, cur, aa, ab, 1);
   mma_frags<T>(acc, fa0, fb0);
-  read_frags<TA, TB>(fa0, fb0, cur, a_base, b_base, 2);
+  read_frags<TA, TB>(fa0, fb0, cur, aa, ab, 2);
   mma_frags<T>(acc, fa1, fb1);
-  read_frags<TA, TB>(fa1, fb1, cur, a_base, b_base, 3);
+  read_frags<TA, TB>(fa1, fb1, cur, aa, ab, 3);
   mma_frags<T>(acc, fa0, fb0);
-  sched_step<M, R, 8, 8>();  // step 0 with the LDS stores and global loads
+  sched_step<M, R, 0, 0>();  // step 0
   sched_step<M, R, 0, 0>();  // step 1
   sched_step<M, R, 0, 0>();  // step 2
   __builtin_amdgcn_s_setprio(0);
-  __syncthreads();
+  dma_barrier();
   __builtin_amdgcn_s_setprio(1);
-  read_frags<TA, TB>(fa0, fb0, nxt, a_base, b_base, 0);
+  read_frags<TA, TB>(fa0, fb0, nxt, aa, ab, 0);
+  A.load(cur, k_load);
+  B.load(cur + kOperandBytes, k_load);
   mma_frags<T>(acc, fa1, fb1);
-  sched_step<M, R, 0, 0>();  // step 3 under the next slice's first fragment reads
+  sched_step<M, R, 0, 0>();  // step 3 under the next fragment reads and the loads
 }
 
 // The two operands of one output tile.
@@ -366,10 +420,10 @@ template <typename AccT> __device__ __forceinline__ void zero_acc(AccT& acc) {
 // C = A[tile rows][K] x B[tile rows][K]^T over ktiles K slices each (ktiles even: callers
 // round up, the extra slice reading zeros past K); mk(i) returns the
 // operands of its i-th tile and epi(i, acc) consumes that tile's accumulators.  Two LDS
-// stages and two register staging sets: global loads run two K slices ahead of the MFMAs
-// and LDS stores one slice ahead, with one barrier per slice.  The load stream runs across
-// tile boundaries (the first slices of tile i + 1 load while tile i finishes), so only the
-// epilogue separates consecutive tiles' MFMAs.  Loads past the last tile read zeros.
+// stages filled by DMA loads one slice ahead of the MFMAs, one barrier per slice.  The
+// load stream runs across tile boundaries (the first slices of tile i + 1 load while tile
+// i finishes), so only the epilogue separates consecutive tiles' MFMAs.  Loads past the
+// last tile read zeros.
 template <typename T, typename MakeOps, typename Epi>
 __device__ __forceinline__ void gemm_run(char* lds, int count, int ktiles, const MakeOps& mk, Epi&& epi) {
   using O = decltype(mk(0));
@@ -377,13 +431,15 @@ __device__ __forceinline__ void gemm_run(char* lds, int count, int ktiles, const
   using TB = typename O::TB;
   constexpr int BK = kStageK<T>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int a_off = TA::frag_base((wave >> 2) * kWaveM, lane);
-  const int b_off = TB::frag_base((wave & 3) * kWaveN, lane);
+  FragAddr aa, ab;
+  TA::frag_addrs(aa, (wave >> 2) * kWaveM, lane);
+  TB::frag_addrs(ab, (wave & 3) * kWaveN, lane);
   f32x16 acc[kBM][kBN];
   zero_acc(acc);
 
-  Stage4 a0, b0, a1, b1;
   u32x4 fa0[kBM], fb0[kBN], fa1[kBM], fb1[kBN];
+  char* s0 = lds;
+  char* s1 = lds + kStageBytes;
   O ld = mk(0);       // operands of the next slice to load,
   int lt = 0, lk = 0;  // its tile and K slice
   auto advance = [&]() {
@@ -392,24 +448,20 @@ __device__ __forceinline__ void gemm_run(char* lds, int count, int ktiles, const
       ld = mk(++lt);
     }
   };
-  ld.a.load(a0, 0);
-  ld.b.load(b0, 0);
+  ld.a.load(s0, 0);
+  ld.b.load(s0 + kOperandBytes, 0);
   advance();
-  ld.a.load(a1, lk * BK);
-  ld.b.load(b1, lk * BK);
+  ld.a.load(s1, lk * BK);
+  ld.b.load(s1 + kOperandBytes, lk * BK);
   advance();
-  ld.a.store(a0, lds);
-  ld.b.store(b0, lds + kOperandBytes);
-  __syncthreads();
-  read_frags<TA, TB>(fa0, fb0, lds, a_off, b_off, 0);
-  char* s0 = lds;
-  char* s1 = lds + kStageBytes;
+  dma_barrier();
+  read_frags<TA, TB>(fa0, fb0, s0, aa, ab, 0);
   int ct = 0, ck = 0;  // tile and K slice being multiplied
   const int total = count * ktiles;
   for (int g = 0; g < total; g += 2) {
-    gemm_slice<T>(acc, s0, s1, ld.a, ld.b, a1, b1, a0, b0, fa0, fb0, fa1, fb1, a_off, b_off, lk * BK);
+    gemm_slice<T>(acc, s0, s1, ld.a, ld.b, fa0, fb0, fa1, fb1, aa, ab, lk * BK);
     advance();
-    gemm_slice<T>(acc, s1, s0, ld.a, ld.b, a0, b0, a1, b1, fa0, fb0, fa1, fb1, a_off, b_off, lk * BK);
+    gemm_slice<T>(acc, s1, s0, ld.a, ld.b, fa0, fb0, fa1, fb1, aa, ab, lk * BK);
     advance();
     ck += 2;
     if (ck == ktiles) {
