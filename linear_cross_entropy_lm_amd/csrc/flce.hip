@@ -55,9 +55,12 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 512;                      // eight wave64s, two per SIMD
+constexpr int kWaves = 8;                          // wave64s per workgroup, two per SIMD
+constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 256;                         // output tile edge
-constexpr int kWaveM = 128, kWaveN = 64;           // per-wave output block (2 x 4 waves)
+constexpr int kWaveM = 128;                        // per-wave output block: kWaveM x kWaveN,
+constexpr int kWaveN = kTile * kTile / kWaveM / kWaves;  // waves laid out 2 x (kWaves / 2)
+constexpr int kWavesN = kTile / kWaveN;
 constexpr int kBM = kWaveM / 32, kBN = kWaveN / 32;  // 32 x 32 MFMA blocks per wave
 constexpr int kKBytes = 128;                       // K bytes per tile element per stage
 constexpr int kOperandBytes = kTile * kKBytes;     // one operand, one stage: 32 KiB
@@ -296,9 +299,9 @@ template <> struct MNTile<float> {
 
 // ---------------------------------------------------------------------------------
 // MFMA over LDS stages.  32 x 32 block operands: lane l supplies row (l & 31) and the
-// K elements of 16-byte chunk 2 * ks + (l >> 5).  Wave w = 4 wm + wn owns output rows
-// 128 wm .. +127 and columns 64 wn .. +63; its result element acc[i][j][r] is
-// C[128 wm + 32 i + 8 (r >> 2) + 4 (l >> 5) + (r & 3)][64 wn + 32 j + (l & 31)].
+// K elements of 16-byte chunk 2 * ks + (l >> 5).  Wave w = kWavesN wm + wn owns output
+// rows kWaveM wm .. + kWaveM - 1 and columns kWaveN wn .. + kWaveN - 1; its result element
+// acc[i][j][r] is C[kWaveM wm + 32 i + 8 (r >> 2) + 4 (l >> 5) + (r & 3)][kWaveN wn + 32 j + (l & 31)].
 // ---------------------------------------------------------------------------------
 
 template <typename T> struct Mfma;
@@ -432,8 +435,8 @@ __device__ __forceinline__ void gemm_run(char* lds, int count, int ktiles, const
   constexpr int BK = kStageK<T>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   FragAddr aa, ab;
-  TA::frag_addrs(aa, (wave >> 2) * kWaveM, lane);
-  TB::frag_addrs(ab, (wave & 3) * kWaveN, lane);
+  TA::frag_addrs(aa, (wave / kWavesN) * kWaveM, lane);
+  TB::frag_addrs(ab, (wave % kWavesN) * kWaveN, lane);
   f32x16 acc[kBM][kBN];
   zero_acc(acc);
 
@@ -510,7 +513,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles(const T* __restrict__ H
   constexpr int BK = kStageK<T>;
   const int ldb = D * (int)sizeof(T);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, t = threadIdx.x;
-  const int wm = wave >> 2, wn = wave & 3, lr = lane & 31, lh = lane >> 5;
+  const int wm = wave / kWavesN, wn = wave % kWavesN, lr = lane & 31, lh = lane >> 5;
   float2* red = reinterpret_cast<float2*>(lds + kLdsBytes);  // [wm][token in tile]
   int64_t lab[kBN];
 #pragma unroll
@@ -529,38 +532,53 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles(const T* __restrict__ H
     const int v0 = (sp + i * splits) * kTile;
     const int vbase = v0 + wm * kWaveM + 4 * lh;  // vocab row of acc[0][j][0] in this lane
     const int vlim = V - vbase;                   // offsets below vlim are real rows
+    const bool full = v0 + kTile <= V;            // workgroup-uniform: no row past V
     float mrow[kBN], srow[kBN];
 #pragma unroll
     for (int j = 0; j < kBN; ++j) {
       const int n = n0 + wn * kWaveN + 32 * j + lr;
-      const int64_t rel = lab[j] - vbase;
-      float m = -__builtin_inff(), zl = 0.f;
-      bool hit = false;
-#pragma unroll
-      for (int ii = 0; ii < kBM; ++ii)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = 32 * ii + 8 * (r >> 2) + (r & 3);
-          const float z = acc[ii][j][r];
-          if (off < vlim) m = fmaxf(m, z);
-          if (rel == off) {
-            zl = z;
-            hit = true;
-          }
-        }
-      float sum = 0.f;
-      if (m != -__builtin_inff()) {
-        const float mb = m * kLog2e;
+      float m = -__builtin_inff();
+      if (full) {
 #pragma unroll
         for (int ii = 0; ii < kBM; ++ii)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int off = 32 * ii + 8 * (r >> 2) + (r & 3);
-            if (off < vlim) sum += hw_exp2(__builtin_fmaf(acc[ii][j][r], kLog2e, -mb));
-          }
+          for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[ii][j][r]);
+      } else {
+#pragma unroll
+        for (int ii = 0; ii < kBM; ++ii)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * ii + 8 * (r >> 2) + (r & 3) < vlim) m = fmaxf(m, acc[ii][j][r]);
+      }
+      float sum = 0.f;
+      if (m != -__builtin_inff()) {
+        const float mb = m * kLog2e;
+        if (full) {
+#pragma unroll
+          for (int ii = 0; ii < kBM; ++ii)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sum += hw_exp2(__builtin_fmaf(acc[ii][j][r], kLog2e, -mb));
+        } else {
+#pragma unroll
+          for (int ii = 0; ii < kBM; ++ii)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (32 * ii + 8 * (r >> 2) + (r & 3) < vlim) sum += hw_exp2(__builtin_fmaf(acc[ii][j][r], kLog2e, -mb));
+        }
       }
       lse_merge(m, sum, __shfl_xor(m, 32), __shfl_xor(sum, 32));
-      if (hit && n < N) zlab[n] = zl;
+      // The label logit: the lane's rows are the offsets 32 ii + 8 q + e (e < 4) from vbase,
+      // so only a lane whose label lands on one of them searches its accumulators.
+      const int64_t rel = lab[j] - vbase;
+      if (n < N && rel >= 0 && rel < kWaveM && (rel & 4) == 0) {
+        float zl = 0.f;
+#pragma unroll
+        for (int ii = 0; ii < kBM; ++ii)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (rel == 32 * ii + 8 * (r >> 2) + (r & 3)) zl = acc[ii][j][r];
+        zlab[n] = zl;
+      }
       mrow[j] = m;
       srow[j] = sum;
     }
@@ -700,7 +718,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dz(const T* __restrict__ H, c
   const int ldb = D * (int)sizeof(T);
   const int tiles = ((vc_act + kTile - 1) / kTile) * n_tiles_t;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 2, wn = wave & 3, lr = lane & 31, lh = lane >> 5;
+  const int wm = wave / kWavesN, wn = wave % kWavesN, lr = lane & 31, lh = lane >> 5;
   auto mk = [&](int i) {
     const int b = my_tile(i);
     const int vl0 = (b / n_tiles_t) * kTile, tl0 = (b % n_tiles_t) * kTile;
@@ -712,6 +730,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dz(const T* __restrict__ H, c
     const int vl0 = (b / n_tiles_t) * kTile, tl0 = (b % n_tiles_t) * kTile;
     const int vb = vl0 + wm * kWaveM + 4 * lh;  // chunk-local vocab row of acc[0][j][0]
     const int vlim = vc_act - vb;
+    const bool full = vl0 + kTile <= vc_act;  // workgroup-uniform: no row past the chunk
 #pragma unroll
     for (int j = 0; j < kBN; ++j) {
       const int nl = tl0 + wn * kWaveN + 32 * j + lr;
@@ -725,20 +744,41 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dz(const T* __restrict__ H, c
         rel = lb < 0 ? -1 : lb - v0c - vb;
       }
       T* out = slab + (int64_t)nl * ld_slab + vb;
+      if (full) {
 #pragma unroll
-      for (int ii = 0; ii < kBM; ++ii)
+        for (int ii = 0; ii < kBM; ++ii)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float d[4];
+          for (int q = 0; q < 4; ++q) {
+            float d[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int off = 32 * ii + 8 * q + e;
-            float p = hw_exp2(__builtin_fmaf(acc[ii][j][4 * q + e], kLog2e, -L2));
-            if (off == rel) p -= 1.f;
-            d[e] = off < vlim ? p * cf : 0.f;
+            for (int e = 0; e < 4; ++e) d[e] = hw_exp2(__builtin_fmaf(acc[ii][j][4 * q + e], kLog2e, -L2)) * cf;
+            store4<T>(out + 32 * ii + 8 * q, d);
           }
-          store4<T>(out + 32 * ii + 8 * q, d);
-        }
+      } else {
+#pragma unroll
+        for (int ii = 0; ii < kBM; ++ii)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float d[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float p = hw_exp2(__builtin_fmaf(acc[ii][j][4 * q + e], kLog2e, -L2));
+              d[e] = 32 * ii + 8 * q + e < vlim ? p * cf : 0.f;
+            }
+            store4<T>(out + 32 * ii + 8 * q, d);
+          }
+      }
+      // The one-hot term: the lane holding the label's row (offsets 32 ii + 8 q + e, e < 4)
+      // rewrites that element as (p - 1) * cf after the plain store above.
+      if (rel >= 0 && rel < kWaveM && (rel & 4) == 0) {
+        float z = 0.f;
+#pragma unroll
+        for (int ii = 0; ii < kBM; ++ii)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (rel == 32 * ii + 8 * (r >> 2) + (r & 3)) z = acc[ii][j][r];
+        out[rel] = from_f32<T>((hw_exp2(__builtin_fmaf(z, kLog2e, -L2)) - 1.f) * cf);
+      }
     }
   };
   gemm_run<T>(lds, my_tile_count(tiles), even_slices<T>(D), mk, epi);
@@ -761,7 +801,7 @@ template <typename TO>
 __device__ __forceinline__ void tile_out(const f32x16 (&acc)[kBM][kBN], const float* prev, TO* out, int ld,
                                          int rows_ok, int cols_ok) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 2, wn = wave & 3, lr = lane & 31, lh = lane >> 5;
+  const int wm = wave / kWavesN, wn = wave % kWavesN, lr = lane & 31, lh = lane >> 5;
   const int rows = rows_ok < kTile ? rows_ok : kTile;
   const u32 span = (u32)(rows - 1) * (u32)ld + (u32)cols_ok;  // elements inside the tile's range
   const __amdgpu_buffer_rsrc_t rp = make_rsrc(prev ? (const void*)prev : (const void*)out, span * 4u);
