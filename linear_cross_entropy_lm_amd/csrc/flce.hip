@@ -324,21 +324,38 @@ template <> struct Mfma<float> {
   }
 };
 
+// Fragment read order: A and B blocks interleaved (A0, B0, A1, B1, ...), the longer list's
+// tail last.  rank_a / rank_b give each block's position in that order.
+constexpr int rank_a(int i) { return i < kBN ? 2 * i : kBN + i; }
+constexpr int rank_b(int j) { return j < kBM ? 2 * j + 1 : kBM + j; }
+constexpr int max_i(int a, int b) { return a > b ? a : b; }
+
 template <typename TA, typename TB>
 __device__ __forceinline__ void read_frags(u32x4 (&fa)[kBM], u32x4 (&fb)[kBN], const char* stage, const FragAddr& aa,
                                            const FragAddr& ab, int ks) {
 #pragma unroll
-  for (int i = 0; i < kBM; ++i) fa[i] = TA::frag(stage, aa, i, ks);
+  for (int r = 0; r < kBM + kBN; ++r) {
 #pragma unroll
-  for (int j = 0; j < kBN; ++j) fb[j] = TB::frag(stage + kOperandBytes, ab, j, ks);
+    for (int i = 0; i < kBM; ++i)
+      if (rank_a(i) == r) fa[i] = TA::frag(stage, aa, i, ks);
+#pragma unroll
+    for (int j = 0; j < kBN; ++j)
+      if (rank_b(j) == r) fb[j] = TB::frag(stage + kOperandBytes, ab, j, ks);
+  }
 }
 
+// The products of one K step, ordered by the later of their two fragments' read positions,
+// so the first products need only the first fragments read and every read has most of a
+// step of MFMAs to land.
 template <typename T>
 __device__ __forceinline__ void mma_frags(f32x16 (&acc)[kBM][kBN], const u32x4 (&fa)[kBM], const u32x4 (&fb)[kBN]) {
 #pragma unroll
-  for (int i = 0; i < kBM; ++i)
+  for (int r = 0; r < kBM + kBN; ++r)
 #pragma unroll
-    for (int j = 0; j < kBN; ++j) Mfma<T>::run(acc[i][j], fa[i], fb[j]);
+    for (int i = 0; i < kBM; ++i)
+#pragma unroll
+      for (int j = 0; j < kBN; ++j)
+        if (max_i(rank_a(i), rank_b(j)) == r) Mfma<T>::run(acc[i][j], fa[i], fb[j]);
 }
 
 // Scheduling masks for __builtin_amdgcn_sched_group_barrier.
@@ -426,7 +443,8 @@ template <typename AccT> __device__ __forceinline__ void zero_acc(AccT& acc) {
 // stages filled by DMA loads one slice ahead of the MFMAs, one barrier per slice.  The
 // load stream runs across tile boundaries (the first slices of tile i + 1 load while tile
 // i finishes), so only the epilogue separates consecutive tiles' MFMAs.  Loads past the
-// last tile read zeros.
+// last tile read zeros; the driver drains them before returning, so no DMA load is still
+// writing LDS when the workgroup ends.
 template <typename T, typename MakeOps, typename Epi>
 __device__ __forceinline__ void gemm_run(char* lds, int count, int ktiles, const MakeOps& mk, Epi&& epi) {
   using O = decltype(mk(0));
@@ -459,21 +477,18 @@ __device__ __forceinline__ void gemm_run(char* lds, int count, int ktiles, const
   advance();
   dma_barrier();
   read_frags<TA, TB>(fa0, fb0, s0, aa, ab, 0);
-  int ct = 0, ck = 0;  // tile and K slice being multiplied
-  const int total = count * ktiles;
-  for (int g = 0; g < total; g += 2) {
-    gemm_slice<T>(acc, s0, s1, ld.a, ld.b, fa0, fb0, fa1, fb1, aa, ab, lk * BK);
-    advance();
-    gemm_slice<T>(acc, s1, s0, ld.a, ld.b, fa0, fb0, fa1, fb1, aa, ab, lk * BK);
-    advance();
-    ck += 2;
-    if (ck == ktiles) {
-      epi(ct++, acc);
-      zero_acc(acc);
-      ck = 0;
+  for (int t = 0; t < count; ++t) {
+    for (int k = 0; k < ktiles; k += 2) {
+      gemm_slice<T>(acc, s0, s1, ld.a, ld.b, fa0, fb0, fa1, fb1, aa, ab, lk * BK);
+      advance();
+      gemm_slice<T>(acc, s1, s0, ld.a, ld.b, fa0, fb0, fa1, fb1, aa, ab, lk * BK);
+      advance();
     }
+    epi(t, acc);
+    zero_acc(acc);
   }
   __builtin_amdgcn_s_setprio(0);
+  __builtin_amdgcn_s_waitcnt(0x0f70);
 }
 
 // Tiles of a 2-D grid handed out round-robin to `grid` persistent workgroups.
