@@ -31,7 +31,7 @@
 //                 (workgroup, token), and the label logit (compare in the epilogue).
 //   fwd_combine   merge partials per token in fixed order -> lse, row loss; block sums.
 //   fwd_finalize  fixed-order sum of block sums -> loss, N_valid, dev_status.
-//   bwd_prep      per-row lse*log2(e), g/N_valid (0 for ignored rows), label.
+//   bwd_prep      per row: c = g/N_valid (0 for ignored rows), lse log2(e) - log2|c|, label.
 //   bwd_dz        recompute a Z^T tile of one (vocab chunk, token chunk), form
 //                 dz = (p - onehot) * g/N_valid, write it to the chunk slab.
 //   bwd_dh        dH[chunk rows] (+)= slab x W[vocab chunk]   (fp32 accumulator)
@@ -497,6 +497,23 @@ __device__ __forceinline__ int my_tile_count(int tiles) {
 }
 __device__ __forceinline__ int my_tile(int i) { return (int)blockIdx.x + i * (int)gridDim.x; }
 
+// Tile t of a rows x cols grid -> (row, col).  Workgroups are dispatched to the eight XCDs
+// (each with its own L2) round-robin by index, and a persistent workgroup's tiles t, t + G,
+// ... keep t mod 8 when G is a multiple of 8, so the tiles with t mod 8 = x run on XCD x.
+// They are given one contiguous range of positions, and positions run down groups of four
+// rows, column by column: the 32 tiles an XCD runs at once form a 4 x 8 block, whose K
+// slices come from 12 operand tiles instead of the 2 + 16 of a row-major order.  A
+// bijection for any tile count.
+__device__ __forceinline__ void tile_rc(int t, int rows, int cols, int& r, int& c) {
+  const int T = rows * cols, x = t & 7;
+  const int p = x * (T >> 3) + (x < (T & 7) ? x : (T & 7)) + (t >> 3);
+  constexpr int Gh = 4;
+  const int g = p / (Gh * cols), w = p - g * Gh * cols;
+  const int h = rows - g * Gh < Gh ? rows - g * Gh : Gh;
+  r = g * Gh + w % h;
+  c = w / h;
+}
+
 // K slices of a contraction of length K, rounded up to an even count for gemm_run.
 template <typename T> __device__ __forceinline__ int even_slices(int K) {
   const int k = (K + kStageK<T> - 1) / kStageK<T>;
@@ -697,7 +714,7 @@ __global__ __launch_bounds__(256) void fwd_finalize(const double* __restrict__ b
 
 __global__ __launch_bounds__(256) void bwd_prep(const float* __restrict__ lse, const int64_t* __restrict__ y,
                                                 const int32_t* __restrict__ n_valid, const float* __restrict__ grad,
-                                                int N, int V, int64_t ignore_index, float* __restrict__ lse2,
+                                                int N, int V, int64_t ignore_index, float* __restrict__ e2,
                                                 float* __restrict__ coef, int* __restrict__ lab) {
   const int n = blockIdx.x * 256 + threadIdx.x;
   if (n >= N) return;
@@ -706,8 +723,11 @@ __global__ __launch_bounds__(256) void bwd_prep(const float* __restrict__ lse, c
   const float s = nv > 0 ? g / (float)nv : 0.f;
   const int64_t l = y[n];
   const bool ok = l != ignore_index && l >= 0 && l < V;
-  lse2[n] = lse[n] * kLog2e;
-  coef[n] = ok ? s : 0.f;
+  const float c = ok ? s : 0.f;
+  // dz = c * exp(z - lse) = sign(c) * 2^(z log2(e) - e2) with e2 = lse log2(e) - log2|c|;
+  // e2 = +inf gives exactly 0 for rows with c = 0.
+  e2[n] = c != 0.f ? lse[n] * kLog2e - hw_log2(fabsf(c)) : __builtin_inff();
+  coef[n] = c;
   lab[n] = ok ? (int)l : -1;
 }
 
@@ -720,12 +740,32 @@ template <> __device__ __forceinline__ void store4<float>(float* p, const float 
   *reinterpret_cast<float4*>(p) = make_float4(d[0], d[1], d[2], d[3]);
 }
 
+// Two floats to packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32 pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(u32, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// store4 of the values with their sign bits xor-ed with sgn (0 or 0x80000000).
+template <typename T> __device__ __forceinline__ void store4_signed(T* p, const float (&d)[4], u32 sgn);
+template <> __device__ __forceinline__ void store4_signed<u16>(u16* p, const float (&d)[4], u32 sgn) {
+  const u32 m = sgn | (sgn >> 16);
+  *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(d[0], d[1]) ^ m, pack_bf16x2(d[2], d[3]) ^ m};
+}
+template <> __device__ __forceinline__ void store4_signed<float>(float* p, const float (&d)[4], u32 sgn) {
+  u32x4 v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = __builtin_bit_cast(u32, d[e]) ^ sgn;
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
 // dz tiles of one (vocab chunk, token chunk); slab is [token in chunk][vocab in chunk].
-// Persistent: tile b = (vt, tt) = (b / n_tiles_t, b % n_tiles_t), handed out round-robin.
+// Persistent: tile b = (vt, tt) in the order of tile_rc, handed out round-robin.
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dz(const T* __restrict__ H, const T* __restrict__ W, int D,
                                                        int v0c, int vc_act, int t0c, int tc_act, int n_tiles_t,
-                                                       const float* __restrict__ lse2, const float* __restrict__ coef,
+                                                       const float* __restrict__ e2, const float* __restrict__ coef,
                                                        const int* __restrict__ lab, T* __restrict__ slab,
                                                        int ld_slab) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
@@ -734,30 +774,35 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dz(const T* __restrict__ H, c
   const int tiles = ((vc_act + kTile - 1) / kTile) * n_tiles_t;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN, lr = lane & 31, lh = lane >> 5;
+  const int n_vt = (vc_act + kTile - 1) / kTile;
   auto mk = [&](int i) {
-    const int b = my_tile(i);
-    const int vl0 = (b / n_tiles_t) * kTile, tl0 = (b % n_tiles_t) * kTile;
+    int vt, tt;
+    tile_rc(my_tile(i), n_vt, n_tiles_t, vt, tt);
+    const int vl0 = vt * kTile, tl0 = tt * kTile;
     return Ops<KTile<T>, KTile<T>>{KTile<T>(W + (int64_t)(v0c + vl0) * D, ldb, vc_act - vl0, D),
                                    KTile<T>(H + (int64_t)(t0c + tl0) * D, ldb, tc_act - tl0, D)};
   };
   auto epi = [&](int i, const f32x16 (&acc)[kBM][kBN]) {
-    const int b = my_tile(i);
-    const int vl0 = (b / n_tiles_t) * kTile, tl0 = (b % n_tiles_t) * kTile;
+    int vt, tt;
+    tile_rc(my_tile(i), n_vt, n_tiles_t, vt, tt);
+    const int vl0 = vt * kTile, tl0 = tt * kTile;
     const int vb = vl0 + wm * kWaveM + 4 * lh;  // chunk-local vocab row of acc[0][j][0]
     const int vlim = vc_act - vb;
     const bool full = vl0 + kTile <= vc_act;  // workgroup-uniform: no row past the chunk
 #pragma unroll
     for (int j = 0; j < kBN; ++j) {
       const int nl = tl0 + wn * kWaveN + 32 * j + lr;
-      float L2 = 0.f, cf = 0.f;
+      float L2 = __builtin_inff(), cf = 0.f;  // rows past the chunk: exp2(-inf) = 0
       int rel = -1;
       if (nl < tc_act) {
         const int n = t0c + nl;
-        L2 = lse2[n];
+        L2 = e2[n];
         cf = coef[n];
         const int lb = lab[n];
         rel = lb < 0 ? -1 : lb - v0c - vb;
       }
+      // L2 already holds lse log2(e) - log2|cf|: the element is sign(cf) 2^(z log2(e) - L2).
+      const u32 sgn = __builtin_bit_cast(u32, cf) & 0x80000000u;
       T* out = slab + (int64_t)nl * ld_slab + vb;
       if (full) {
 #pragma unroll
@@ -766,8 +811,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dz(const T* __restrict__ H, c
           for (int q = 0; q < 4; ++q) {
             float d[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) d[e] = hw_exp2(__builtin_fmaf(acc[ii][j][4 * q + e], kLog2e, -L2)) * cf;
-            store4<T>(out + 32 * ii + 8 * q, d);
+            for (int e = 0; e < 4; ++e) d[e] = hw_exp2(__builtin_fmaf(acc[ii][j][4 * q + e], kLog2e, -L2));
+            store4_signed<T>(out + 32 * ii + 8 * q, d, sgn);
           }
       } else {
 #pragma unroll
@@ -778,13 +823,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dz(const T* __restrict__ H, c
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const float p = hw_exp2(__builtin_fmaf(acc[ii][j][4 * q + e], kLog2e, -L2));
-              d[e] = 32 * ii + 8 * q + e < vlim ? p * cf : 0.f;
+              d[e] = 32 * ii + 8 * q + e < vlim ? p : 0.f;
             }
-            store4<T>(out + 32 * ii + 8 * q, d);
+            store4_signed<T>(out + 32 * ii + 8 * q, d, sgn);
           }
       }
       // The one-hot term: the lane holding the label's row (offsets 32 ii + 8 q + e, e < 4)
-      // rewrites that element as (p - 1) * cf after the plain store above.
+      // rewrites that element as (p - 1) cf after the plain store above.
       if (rel >= 0 && rel < kWaveM && (rel & 4) == 0) {
         float z = 0.f;
 #pragma unroll
@@ -792,7 +837,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dz(const T* __restrict__ H, c
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             if (rel == 32 * ii + 8 * (r >> 2) + (r & 3)) z = acc[ii][j][r];
-        out[rel] = from_f32<T>((hw_exp2(__builtin_fmaf(z, kLog2e, -L2)) - 1.f) * cf);
+        const float pc = __builtin_bit_cast(float, __builtin_bit_cast(u32, hw_exp2(__builtin_fmaf(z, kLog2e, -L2))) ^ sgn);
+        out[rel] = from_f32<T>(pc - cf);
       }
     }
   };
@@ -856,7 +902,7 @@ __device__ __forceinline__ void tile_out(const f32x16 (&acc)[kBM][kBN], const fl
 }
 
 // dH rows of one token chunk (+)= slab x W[vocab chunk]; C[n][d].  Persistent over tiles
-// b = (mt, dt) = (b / n_tiles_d, b % n_tiles_d).  ACCUM: add the fp32 partial in dacc;
+// b = (mt, dt) in the order of tile_rc.  ACCUM: add the fp32 partial in dacc;
 // FINAL: write the sum to dH in the output type instead of back to dacc.
 template <typename T, bool ACCUM, bool FINAL>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dh(const T* __restrict__ slab, int ld_slab,
@@ -866,15 +912,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh(const T* __restrict__ slab
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   const int es = (int)sizeof(T);
   const int tiles = ((tc_act + kTile - 1) / kTile) * n_tiles_d;
+  const int n_mt = (tc_act + kTile - 1) / kTile;
   auto mk = [&](int i) {
-    const int b = my_tile(i);
-    const int nl0 = (b / n_tiles_d) * kTile, d0 = (b % n_tiles_d) * kTile;
+    int mt, dt;
+    tile_rc(my_tile(i), n_mt, n_tiles_d, mt, dt);
+    const int nl0 = mt * kTile, d0 = dt * kTile;
     return Ops<KTile<T>, MNTile<T>>{KTile<T>(slab + (int64_t)nl0 * ld_slab, ld_slab * es, tc_act - nl0, vc_act),
                                     MNTile<T>(W + (int64_t)v0c * D + d0, D * es, D - d0, vc_act)};
   };
   auto epi = [&](int i, const f32x16 (&acc)[kBM][kBN]) {
-    const int b = my_tile(i);
-    const int nl0 = (b / n_tiles_d) * kTile, d0 = (b % n_tiles_d) * kTile;
+    int mt, dt;
+    tile_rc(my_tile(i), n_mt, n_tiles_d, mt, dt);
+    const int nl0 = mt * kTile, d0 = dt * kTile;
     float* acc_tile = dacc + (int64_t)nl0 * D + d0;
     const float* prev = ACCUM ? acc_tile : nullptr;
     if constexpr (FINAL)
@@ -886,7 +935,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh(const T* __restrict__ slab
 }
 
 // dW rows of one vocab chunk (+)= slab^T x H[token chunk]; C[v][d].  Persistent over tiles
-// b = (mt, dt) = (b / n_tiles_d, b % n_tiles_d).
+// b = (vt, dt) in the order of tile_rc.
 template <typename T, bool ACCUM>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dw(const T* __restrict__ slab, int ld_slab,
                                                        const T* __restrict__ H, int D, int t0c, int tc_act,
@@ -895,15 +944,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dw(const T* __restrict__ slab
   constexpr int BK = kStageK<T>;
   const int es = (int)sizeof(T);
   const int tiles = ((vc_act + kTile - 1) / kTile) * n_tiles_d;
+  const int n_vt = (vc_act + kTile - 1) / kTile;
   auto mk = [&](int i) {
-    const int b = my_tile(i);
-    const int vl0 = (b / n_tiles_d) * kTile, d0 = (b % n_tiles_d) * kTile;
+    int vt, dt;
+    tile_rc(my_tile(i), n_vt, n_tiles_d, vt, dt);
+    const int vl0 = vt * kTile, d0 = dt * kTile;
     return Ops<MNTile<T>, MNTile<T>>{MNTile<T>(slab + vl0, ld_slab * es, ld_slab - vl0, tc_act),
                                      MNTile<T>(H + (int64_t)t0c * D + d0, D * es, D - d0, tc_act)};
   };
   auto epi = [&](int i, const f32x16 (&acc)[kBM][kBN]) {
-    const int b = my_tile(i);
-    const int vl0 = (b / n_tiles_d) * kTile, d0 = (b % n_tiles_d) * kTile;
+    int vt, dt;
+    tile_rc(my_tile(i), n_vt, n_tiles_d, vt, dt);
+    const int vl0 = vt * kTile, d0 = dt * kTile;
     float* tile = dW + (int64_t)(v0c + vl0) * D + d0;
     tile_out<float>(acc, ACCUM ? tile : nullptr, tile, D, vc_act - vl0, D - d0);
   };
@@ -965,7 +1017,7 @@ FwdLayout fwd_layout(int64_t N, int64_t V) {
 
 struct BwdLayout {
   int64_t tc, vc;  // chunk sizes (multiples of 256)
-  size_t lse2, coef, lab, slab, dacc, total;
+  size_t e2, coef, lab, slab, dacc, total;
 };
 
 BwdLayout bwd_layout(int64_t N, int64_t D, int dtype, int64_t tc, int64_t vc) {
@@ -973,7 +1025,7 @@ BwdLayout bwd_layout(int64_t N, int64_t D, int dtype, int64_t tc, int64_t vc) {
   L.tc = tc;
   L.vc = vc;
   size_t off = 0;
-  L.lse2 = off;
+  L.e2 = off;
   off += region((size_t)N * 4);
   L.coef = off;
   off += region((size_t)N * 4);
@@ -1050,7 +1102,7 @@ template <typename T>
 flce_status backward_impl(const T* H, const T* W, const int64_t* y, const float* lse, const int32_t* n_valid,
                           const float* grad, int N, int D, int V, int dtype, int64_t ignore_index, T* dH,
                           float* dW, char* ws, const BwdLayout& L, hipStream_t s) {
-  float* lse2 = reinterpret_cast<float*>(ws + L.lse2);
+  float* e2 = reinterpret_cast<float*>(ws + L.e2);
   float* coef = reinterpret_cast<float*>(ws + L.coef);
   int* lab = reinterpret_cast<int*>(ws + L.lab);
   T* slab = reinterpret_cast<T*>(ws + L.slab);
@@ -1058,7 +1110,7 @@ flce_status backward_impl(const T* H, const T* W, const int64_t* y, const float*
   const int ld_slab = (int)L.vc;
   const int n_td = (int)ceil_div(D, kTile);
   (void)hipGetLastError();
-  bwd_prep<<<dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, s>>>(lse, y, n_valid, grad, N, V, ignore_index, lse2,
+  bwd_prep<<<dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, s>>>(lse, y, n_valid, grad, N, V, ignore_index, e2,
                                                                   coef, lab);
   // Chunks of whole 256-row tiles, spread evenly: chunk i of n covers tiles
   // [i T / n, (i + 1) T / n) of the T tiles, never more than the workspace's chunk size.
@@ -1077,7 +1129,7 @@ flce_status backward_impl(const T* H, const T* W, const int64_t* y, const float*
       const int v1c = (int)((vi + 1) * v_tiles / n_vc * kTile);
       const int vc_act = (v1c < V ? v1c : V) - v0c;
       const int n_vt = (int)ceil_div(vc_act, kTile);
-      bwd_dz<T><<<dim3(grid(n_vt * n_tt)), dim3(kThreads), 0, s>>>(H, W, D, v0c, vc_act, t0c, tc_act, n_tt, lse2,
+      bwd_dz<T><<<dim3(grid(n_vt * n_tt)), dim3(kThreads), 0, s>>>(H, W, D, v0c, vc_act, t0c, tc_act, n_tt, e2,
                                                                    coef, lab, slab, ld_slab);
       const dim3 gh(grid(n_tt * n_td)), gw(grid(n_vt * n_td)), blk(kThreads);
       const bool acc_dh = vi > 0, fin = dacc && vi == n_vc - 1;
