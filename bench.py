@@ -5,7 +5,8 @@
 One step = flce_forward + flce_backward over one batch of synthetic input already
 resident in HBM (loss, lse, dH, dW all produced).  Prints one JSON line.
 
-value        tokens per second (N / step time), the whole job on one GPU
+value        tokens per second (N / mean step time over the timed steps), the whole job
+             on one GPU; per-step median/min/max from events around each step
 roofline     the forward logit kernel (fwd_tiles): 2*N*V*D flop per launch over its
              average duration from HIP events on the launch stream, against the bf16
              dense MFMA peak (2.5 PFLOP/s); traffic from the committed rocprofv3 counter
@@ -50,6 +51,44 @@ def load_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
+def _counter_per_dispatch(csv_dir: str, counter: str, kernel_prefix: str):
+    """Mean value of `counter` over the dispatches of kernels whose name contains
+    kernel_prefix, from a rocprofv3 --pmc --output-format csv directory."""
+    import csv
+    import glob
+    vals = {}
+    for path in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter and kernel_prefix in r["Kernel_Name"]:
+                    vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"no {counter} samples for {kernel_prefix!r} under {csv_dir}")
+    return sum(vals.values()) / len(vals), len(vals)
+
+
+def summarize_counters(root: str, copy_bytes: int) -> dict:
+    """Write the fwd_tiles HBM traffic record from four rocprofv3 --pmc runs under root:
+    F (FETCH_SIZE) and W (WRITE_SIZE) of `bench.py --steps 1 --warmup 0 --no-cpu-baseline`,
+    FC and WC of `bench.py --calibrate-copy copy_bytes`.  Each counter is scaled by what it
+    reads for the copy (copy_bytes read and copy_bytes written)."""
+    fetch, n_f = _counter_per_dispatch(os.path.join(root, "F"), "FETCH_SIZE", "fwd_tiles")
+    write, n_w = _counter_per_dispatch(os.path.join(root, "W"), "WRITE_SIZE", "fwd_tiles")
+    cf, _ = _counter_per_dispatch(os.path.join(root, "FC"), "FETCH_SIZE", "copyBuffer")
+    cw, _ = _counter_per_dispatch(os.path.join(root, "WC"), "WRITE_SIZE", "copyBuffer")
+    f_factor = copy_bytes / (cf * 1024.0)
+    w_factor = copy_bytes / (cw * 1024.0)
+    rec = {"kernel": "fwd_tiles", "workload": "llama3", "source_digest": source_digest(),
+           "fetch_kib_per_launch": fetch, "write_kib_per_launch": write, "launches": [n_f, n_w],
+           "copy_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
+           "fetch_factor": f_factor, "write_factor": w_factor,
+           "hbm_bytes_per_launch": fetch * 1024.0 * f_factor + write * 1024.0 * w_factor}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec
+
+
 def cpu_baseline(inp, rows: int) -> dict:
     import numpy as np
     import oracle
@@ -77,11 +116,18 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3")
-    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run one device-to-device copy of BYTES bytes (counter calibration)")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="only write the fwd_tiles traffic record from rocprofv3 counter runs under DIR "
+                         "(subdirectories F, W, FC, WC); no GPU needed")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     args = ap.parse_args()
+    if args.summarize_counters:
+        print(json.dumps(summarize_counters(args.summarize_counters, args.copy_bytes)), flush=True)
+        return 0
     if args.calibrate_copy:
         import torch
         src = torch.ones(args.calibrate_copy // 4, dtype=torch.float32, device="cuda:0")
@@ -123,12 +169,19 @@ def main() -> int:
         if ev is not None:
             ev[1].record(stream)
         B.flce_backward(H, W, y, lse, nv, None, dH, dW, ws, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # the library allocates nothing: torch's peak over one step stays at what is already held
+    held = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    step()
+    torch.cuda.synchronize()
+    peak_delta = torch.cuda.max_memory_allocated() - held
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
@@ -137,7 +190,8 @@ def main() -> int:
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
-    fwd_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    step_ms = sorted(e[0].elapsed_time(e[2]) for e in evs)
     if int(st.item()) != 0:
         raise RuntimeError("dev_status reports invalid labels")
 
@@ -165,7 +219,11 @@ def main() -> int:
         "useful_flop_frac": 0.75 * flop_step / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
         "fwd_ms": fwd_ms,
         "bwd_ms": ms - fwd_ms,
+        "step_ms_median": step_ms[len(step_ms) // 2],
+        "step_ms_min": step_ms[0],
+        "step_ms_max": step_ms[-1],
         "scratch_bytes": ws_bytes,
+        "torch_peak_alloc_delta_bytes": int(peak_delta),
         "scratch_frac_of_unfused_logits": scratch_fraction(ws_bytes, N, V),
         "loss": float(loss.item()),
         "roofline": {"kernel": "fwd_tiles", "bound": "mfma", "achieved": achieved,

@@ -15,7 +15,7 @@ What it computes (all in fp64, inputs widened exactly from their fp32 / bf16 val
   the max-subtracted normaliser of the same two sections (two passes over a fully
   materialised row; the streaming form the kernels use is deliberately not used here).
 * per-row loss l[n] = lse[n] - z[n, y[n]] (the cross-entropy equation of the "Fused
-  Chunked Cross-Entropy Loss" pillar on the aifetchly page); rows whose label equals
+  Chunked Cross-Entropy Loss" pillar of the second page above); rows whose label equals
   ``ignore_index`` contribute nothing.
 * loss = sum_n l[n] / N_valid, N_valid = number of non-ignored rows.  The page's numpy
   reference divides by the token count; with ignored rows the divisor is the number of
@@ -23,9 +23,9 @@ What it computes (all in fp64, inputs widened exactly from their fp32 / bf16 val
   gives loss 0 and zero gradients.
 * logit gradient dz[n, v] = (softmax(z[n])[v] - [v == y[n]]) * g / N_valid for valid
   rows and 0 for ignored rows (the analytic gradient p - onehot of section 3 of the
-  llm-curso page and of the aifetchly pillar; g is the upstream gradient of the loss).
+  first page and of the second page's pillar; g is the upstream gradient of the loss).
 * dH = dz W and dW = dz^T H: the gradient flows into the hidden states and into the
-  vocabulary weight (section 3 of the llm-curso page names both).
+  vocabulary weight (section 3 of the first page names both).
 
 Rows are processed in blocks of ``row_block`` rows only so that a block's logits fit in
 memory; every row is computed independently from its own full logit vector.

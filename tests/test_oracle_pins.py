@@ -292,7 +292,8 @@ def test_statistical_band_llama2_rows():
 
 
 def test_worked_example_against_closed_form():
-    """The fp32 numpy walk-through of the aifetchly page (2048 tokens, d = 1024,
+    """The fp32 numpy walk-through of "Unsloth Architecture: 5x Faster LLM Training via
+    Triton" (2048 tokens, d = 1024,
     V = 32000, weights 0.02 * randn, no ignored rows, mean over all tokens).
 
     Closed forms: loss ~ ln V + sigma^2/2 (band above) and |dH|_F ~ 0.02 sqrt(D / N),
