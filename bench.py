@@ -210,7 +210,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "dtype": cfg.dtype,
         "data": "synthetic: seeded Gaussian H with unit-RMS rows, W ~ N(0, 0.02^2), uniform labels, "
                 f"{cfg.n_ignored} ignore_index rows",
         "config": {"workload": f"{cfg.name}-shaped lm_head + cross-entropy, fwd+bwd", "N": N, "D": D,

@@ -25,7 +25,12 @@
  *    contiguous: H[N][D], W[V][D] (the nn.Linear weight layout), y[N] int64, lse[N]
  *    fp32, dH[N][D] in the input element type, dW[V][D] fp32.
  *  - dtype FLCE_BF16: H, W, dH are bf16 (raw 16-bit patterns); products accumulate in
- *    fp32; loss, lse and dW are fp32.  dtype FLCE_F32: everything is fp32.
+ *    fp32; loss, lse and dW are fp32.  dtype FLCE_F16: the same with IEEE fp16 for H, W
+ *    and dH (the pages name fp16 next to bf16 as a 16-bit training format).  dtype
+ *    FLCE_F32: everything is fp32.  The logit gradient dz is rounded to the input type
+ *    before the two backward contractions; for fp16, whose range cannot hold dz itself
+ *    (about g / N_valid / V), it is held as dz * 2^14 * N_valid / |g| and the factor is
+ *    divided out in fp32 after each contraction.
  *  - The caller owns and allocates every buffer, including the workspace (device
  *    scratch).  The library allocates nothing, frees nothing and keeps no state between
  *    calls, so its peak scratch memory is exactly workspace_bytes.
@@ -36,7 +41,7 @@
  *    floating-point atomics; a repeated call with the same inputs and the same
  *    workspace_bytes produces bitwise-identical outputs.
  *  - Size limits: 1 <= N, V <= 2^31 - 512, 1 <= D <= 65536; D must be a multiple of
- *    8 (bf16) or 4 (fp32); H, W, dH, dW and workspace must be 16-byte aligned.
+ *    8 (bf16, fp16) or 4 (fp32); H, W, dH, dW and workspace must be 16-byte aligned.
  */
 #ifndef FLCE_H
 #define FLCE_H
@@ -51,14 +56,15 @@ extern "C" {
 typedef enum flce_status {
   FLCE_OK = 0,
   FLCE_ERR_INVALID_ARG = 1, /* null pointer, size < 1 or too large, unknown dtype */
-  FLCE_ERR_ALIGN = 2,       /* misaligned pointer, or D not a multiple of 8 (bf16) / 4 (fp32) */
+  FLCE_ERR_ALIGN = 2,       /* misaligned pointer, or D not a multiple of 8 (bf16, fp16) / 4 (fp32) */
   FLCE_ERR_WORKSPACE = 3,   /* workspace smaller than the call needs */
   FLCE_ERR_HIP = 4          /* a kernel launch failed (hipGetLastError after launching) */
 } flce_status;
 
 typedef enum flce_dtype {
   FLCE_F32 = 0,
-  FLCE_BF16 = 1
+  FLCE_BF16 = 1,
+  FLCE_F16 = 2
 } flce_dtype;
 
 /*
@@ -68,11 +74,12 @@ typedef enum flce_dtype {
  * Forward needs S * N * 8 bytes of (max, sum-exp) partials plus ~4 * N bytes, where
  * S = min(max(256 / ceil(N / 256), 1), ceil(V / 256)) (integer division) is the number
  * of workgroups that share one 256-row token tile.  Backward needs 12 * N bytes of per-row
- * state, a dz slab of tc_pad * vc_pad elements of the input type, and (bf16 only) an
- * fp32 dH accumulator of tc_pad * D floats, where tc_pad and vc_pad are the token and
- * vocabulary chunk sizes: by default min(N, 4096) and min(V, 8192) rounded up to 256,
- * with the vocabulary chunk trimmed in steps of 256 (not below 4096) while the backward
- * workspace exceeds 5% of N * V * 2 bytes.  Every region is rounded up to 256 bytes.
+ * state plus one 256-byte scalar region, a dz slab of tc_pad * vc_pad elements of the
+ * input type, and (16-bit types only) an fp32 dH accumulator of tc_pad * D floats,
+ * where tc_pad and vc_pad are the token and vocabulary chunk sizes: by default
+ * min(N, 4096) and min(V, 8192) rounded up to 256, with the vocabulary chunk trimmed in
+ * steps of 256 (not below 4096) while the backward workspace exceeds 5% of N * V * 2
+ * bytes.  Every region is rounded up to 256 bytes.
  */
 size_t flce_workspace_bytes(int64_t N, int64_t D, int64_t V, int dtype);
 

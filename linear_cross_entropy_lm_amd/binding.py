@@ -15,7 +15,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflce.so")
 
 FLCE_OK, FLCE_ERR_INVALID_ARG, FLCE_ERR_ALIGN, FLCE_ERR_WORKSPACE, FLCE_ERR_HIP = range(5)
-FLCE_F32, FLCE_BF16 = 0, 1
+FLCE_F32, FLCE_BF16, FLCE_F16 = 0, 1, 2
 IGNORE_INDEX = -100
 
 # symbol -> (restype, argtypes), in the order of include/flce.h
@@ -56,9 +56,11 @@ def flce_status_string(code: int) -> str:
 def dtype_code(dtype: torch.dtype) -> int:
     if dtype == torch.bfloat16:
         return FLCE_BF16
+    if dtype == torch.float16:
+        return FLCE_F16
     if dtype == torch.float32:
         return FLCE_F32
-    raise TypeError(f"unsupported element type {dtype} (bf16 or fp32)")
+    raise TypeError(f"unsupported element type {dtype} (bf16, fp16 or fp32)")
 
 
 def flce_workspace_bytes(N: int, D: int, V: int, dtype) -> int:

@@ -31,7 +31,8 @@
 //                 (workgroup, token), and the label logit (compare in the epilogue).
 //   fwd_combine   merge partials per token in fixed order -> lse, row loss; block sums.
 //   fwd_finalize  fixed-order sum of block sums -> loss, N_valid, dev_status.
-//   bwd_prep      per row: c = g/N_valid (0 for ignored rows), lse log2(e) - log2|c|, label.
+//   bwd_prep      per row: c = g/N_valid (0 for ignored rows), the slab scale a (|c|, or 2^14
+//                 for fp16) as e2 = lse log2(e) - log2(a) and sign(c) a, label.
 //   bwd_dz        recompute a Z^T tile of one (vocab chunk, token chunk), form
 //                 dz = (p - onehot) * g/N_valid, write it to the chunk slab.
 //   bwd_dh        dH[chunk rows] (+)= slab x W[vocab chunk]   (fp32 accumulator)
@@ -70,7 +71,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 template <typename T> struct Elem;
-template <> struct Elem<u16> { static constexpr int kPerChunk = 8; };    // bf16 bits
+// Element tags: u16 holds bf16 bits, h16 IEEE fp16 bits, float fp32.
+struct h16 {
+  u16 bits;
+};
+template <> struct Elem<u16> { static constexpr int kPerChunk = 8; };
+template <> struct Elem<h16> { static constexpr int kPerChunk = 8; };
 template <> struct Elem<float> { static constexpr int kPerChunk = 4; };
 template <typename T> constexpr int kStageK = kKBytes / (int)sizeof(T);  // 64 bf16, 32 fp32
 
@@ -96,6 +102,7 @@ __device__ __forceinline__ u32 bf16_rne(float f) {
 
 template <typename T> __device__ __forceinline__ T from_f32(float f);
 template <> __device__ __forceinline__ u16 from_f32<u16>(float f) { return (u16)bf16_rne(f); }
+template <> __device__ __forceinline__ h16 from_f32<h16>(float f) { return h16{__builtin_bit_cast(u16, (_Float16)f)}; }
 template <> __device__ __forceinline__ float from_f32<float>(float f) { return f; }
 
 // ---------------------------------------------------------------------------------
@@ -255,6 +262,12 @@ template <> struct MNTile<u16> {
   }
 };
 
+// fp16 tiles move and transpose exactly like bf16 ones.
+template <> struct MNTile<h16> : MNTile<u16> {
+  __device__ __forceinline__ MNTile(const h16* base, int ld_bytes, int cols_ok, int k_lim)
+      : MNTile<u16>(reinterpret_cast<const u16*>(base), ld_bytes, cols_ok, k_lim) {}
+};
+
 // fp32: LDS holds 32 K rows of 256 floats (1024 bytes, 64 chunks; chunk c in slot
 // c ^ (8 ((k >> 2) & 1))).  The fp32 MFMA takes one K value per lane, so a fragment is four
 // ds_read_b32 of rows 8 ks + 4 (l >> 5) + e, e = 0..3, at the lane's element: the same K
@@ -310,6 +323,13 @@ template <> struct Mfma<u16> {
   static __device__ __forceinline__ void run(f32x16& c, const u32x4& a, const u32x4& b) {
     c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+template <> struct Mfma<h16> {
+  static constexpr int kPerFrag = 1;
+  static __device__ __forceinline__ void run(f32x16& c, const u32x4& a, const u32x4& b) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
 };
 // fp32: the four floats of a chunk feed four K = 2 steps; A and B pair the same floats.
@@ -714,8 +734,9 @@ __global__ __launch_bounds__(256) void fwd_finalize(const double* __restrict__ b
 
 __global__ __launch_bounds__(256) void bwd_prep(const float* __restrict__ lse, const int64_t* __restrict__ y,
                                                 const int32_t* __restrict__ n_valid, const float* __restrict__ grad,
-                                                int N, int V, int64_t ignore_index, float* __restrict__ e2,
-                                                float* __restrict__ coef, int* __restrict__ lab) {
+                                                int N, int V, int64_t ignore_index, float fixed_scale,
+                                                float* __restrict__ e2, float* __restrict__ coef,
+                                                int* __restrict__ lab, float* __restrict__ oscale) {
   const int n = blockIdx.x * 256 + threadIdx.x;
   if (n >= N) return;
   const int nv = *n_valid;
@@ -724,11 +745,15 @@ __global__ __launch_bounds__(256) void bwd_prep(const float* __restrict__ lse, c
   const int64_t l = y[n];
   const bool ok = l != ignore_index && l >= 0 && l < V;
   const float c = ok ? s : 0.f;
-  // dz = c * exp(z - lse) = sign(c) * 2^(z log2(e) - e2) with e2 = lse log2(e) - log2|c|;
-  // e2 = +inf gives exactly 0 for rows with c = 0.
-  e2[n] = c != 0.f ? lse[n] * kLog2e - hw_log2(fabsf(c)) : __builtin_inff();
-  coef[n] = c;
+  // The slab holds dz / s * a with a = |s| (so it holds dz) or a = fixed_scale (fp16, whose
+  // range cannot hold dz itself); the dH and dW epilogues multiply by |s| / a.  Element:
+  // sign(s) a p = sign(s) 2^(z log2(e) - e2) with e2 = lse log2(e) - log2(a), minus
+  // sign(s) a at the label; e2 = +inf gives exactly 0 for rows with c = 0.
+  const float a = fixed_scale > 0.f ? fixed_scale : fabsf(c);
+  e2[n] = c != 0.f ? lse[n] * kLog2e - hw_log2(a) : __builtin_inff();
+  coef[n] = c != 0.f ? __builtin_copysignf(a, c) : 0.f;
   lab[n] = ok ? (int)l : -1;
+  if (n == 0 && oscale) *oscale = fixed_scale > 0.f ? fabsf(s) / fixed_scale : 1.f;
 }
 
 template <typename T> __device__ __forceinline__ void store4(T* p, const float (&d)[4]);
@@ -740,11 +765,19 @@ template <> __device__ __forceinline__ void store4<float>(float* p, const float 
   *reinterpret_cast<float4*>(p) = make_float4(d[0], d[1], d[2], d[3]);
 }
 
-// Two floats to packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
+// Two floats to packed bf16 / fp16, round to nearest even (v_cvt_pk_bf16_f32,
+// v_cvt_pk_f16_f32).
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32 pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(u32, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+__device__ __forceinline__ u32 pack_f16x2(float a, float b) {
+  return __builtin_bit_cast(u32, __builtin_convertvector(f32x2{a, b}, f16x2));
+}
+template <> __device__ __forceinline__ void store4<h16>(h16* p, const float (&d)[4]) {
+  *reinterpret_cast<u32x2*>(p) = u32x2{pack_f16x2(d[0], d[1]), pack_f16x2(d[2], d[3])};
 }
 
 // store4 of the values with their sign bits xor-ed with sgn (0 or 0x80000000).
@@ -752,6 +785,10 @@ template <typename T> __device__ __forceinline__ void store4_signed(T* p, const 
 template <> __device__ __forceinline__ void store4_signed<u16>(u16* p, const float (&d)[4], u32 sgn) {
   const u32 m = sgn | (sgn >> 16);
   *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(d[0], d[1]) ^ m, pack_bf16x2(d[2], d[3]) ^ m};
+}
+template <> __device__ __forceinline__ void store4_signed<h16>(h16* p, const float (&d)[4], u32 sgn) {
+  const u32 m = sgn | (sgn >> 16);
+  *reinterpret_cast<u32x2*>(p) = u32x2{pack_f16x2(d[0], d[1]) ^ m, pack_f16x2(d[2], d[3]) ^ m};
 }
 template <> __device__ __forceinline__ void store4_signed<float>(float* p, const float (&d)[4], u32 sgn) {
   u32x4 v;
@@ -801,7 +838,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dz(const T* __restrict__ H, c
         const int lb = lab[n];
         rel = lb < 0 ? -1 : lb - v0c - vb;
       }
-      // L2 already holds lse log2(e) - log2|cf|: the element is sign(cf) 2^(z log2(e) - L2).
+      // L2 holds lse log2(e) - log2(a), cf = sign(c) a: the element is sign(c) 2^(z log2(e) - L2).
       const u32 sgn = __builtin_bit_cast(u32, cf) & 0x80000000u;
       T* out = slab + (int64_t)nl * ld_slab + vb;
       if (full) {
@@ -852,15 +889,18 @@ template <> __device__ __forceinline__ void bstore<float>(__amdgpu_buffer_rsrc_t
 template <> __device__ __forceinline__ void bstore<u16>(__amdgpu_buffer_rsrc_t r, u32 off, float v) {
   __builtin_amdgcn_raw_buffer_store_b16((u16)bf16_rne(v), r, (int)off, 0, 0);
 }
+template <> __device__ __forceinline__ void bstore<h16>(__amdgpu_buffer_rsrc_t r, u32 off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(u16, (_Float16)v), r, (int)off, 0, 0);
+}
 
-// Write a C[row][col] tile held in acc (layout of gemm_tile): out = acc (+ prev when prev
-// is not null).  `prev` (fp32) and `out` point at the tile's first element, both with a
+// Write a C[row][col] tile held in acc (layout of gemm_run): out = scale acc (+ prev when
+// prev is not null; with scale 1 the fma is exactly acc + prev).  `prev` (fp32) and `out` point at the tile's first element, both with a
 // row pitch of ld elements; rows at or beyond rows_ok fall outside the buffer descriptors
 // (loads read 0, stores are dropped) and columns at or beyond cols_ok are masked.  The
 // previous values of one 32-row band are loaded before any of them is used.
 template <typename TO>
 __device__ __forceinline__ void tile_out(const f32x16 (&acc)[kBM][kBN], const float* prev, TO* out, int ld,
-                                         int rows_ok, int cols_ok) {
+                                         int rows_ok, int cols_ok, float scale) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN, lr = lane & 31, lh = lane >> 5;
   const int rows = rows_ok < kTile ? rows_ok : kTile;
@@ -896,7 +936,7 @@ __device__ __forceinline__ void tile_out(const f32x16 (&acc)[kBM][kBN], const fl
       for (int r = 0; r < 16; ++r) {
         const u32 e = col[j] == kOOB ? kOOB
                                      : (col[j] + (u32)(32 * i + 8 * (r >> 2) + (r & 3)) * (u32)ld) * (u32)sizeof(TO);
-        bstore<TO>(ro, e, acc[i][j][r] + pv[j][r]);
+        bstore<TO>(ro, e, __builtin_fmaf(acc[i][j][r], scale, pv[j][r]));
       }
   }
 }
@@ -908,8 +948,10 @@ template <typename T, bool ACCUM, bool FINAL>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dh(const T* __restrict__ slab, int ld_slab,
                                                        const T* __restrict__ W, int D, int v0c, int vc_act,
                                                        int t0c, int tc_act, int n_tiles_d,
-                                                       float* __restrict__ dacc, T* __restrict__ dH) {
+                                                       float* __restrict__ dacc, T* __restrict__ dH,
+                                                       const float* __restrict__ oscale) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  const float sc = oscale ? *oscale : 1.f;
   const int es = (int)sizeof(T);
   const int tiles = ((tc_act + kTile - 1) / kTile) * n_tiles_d;
   const int n_mt = (tc_act + kTile - 1) / kTile;
@@ -927,9 +969,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh(const T* __restrict__ slab
     float* acc_tile = dacc + (int64_t)nl0 * D + d0;
     const float* prev = ACCUM ? acc_tile : nullptr;
     if constexpr (FINAL)
-      tile_out<T>(acc, prev, dH + (int64_t)(t0c + nl0) * D + d0, D, tc_act - nl0, D - d0);
+      tile_out<T>(acc, prev, dH + (int64_t)(t0c + nl0) * D + d0, D, tc_act - nl0, D - d0, sc);
     else
-      tile_out<float>(acc, prev, acc_tile, D, tc_act - nl0, D - d0);
+      tile_out<float>(acc, prev, acc_tile, D, tc_act - nl0, D - d0, sc);
   };
   gemm_run<T>(lds, my_tile_count(tiles), even_slices<T>(vc_act), mk, epi);
 }
@@ -939,8 +981,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh(const T* __restrict__ slab
 template <typename T, bool ACCUM>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dw(const T* __restrict__ slab, int ld_slab,
                                                        const T* __restrict__ H, int D, int t0c, int tc_act,
-                                                       int v0c, int vc_act, int n_tiles_d, float* __restrict__ dW) {
+                                                       int v0c, int vc_act, int n_tiles_d, float* __restrict__ dW,
+                                                       const float* __restrict__ oscale) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  const float sc = oscale ? *oscale : 1.f;
   constexpr int BK = kStageK<T>;
   const int es = (int)sizeof(T);
   const int tiles = ((vc_act + kTile - 1) / kTile) * n_tiles_d;
@@ -957,7 +1001,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dw(const T* __restrict__ slab
     tile_rc(my_tile(i), n_vt, n_tiles_d, vt, dt);
     const int vl0 = vt * kTile, d0 = dt * kTile;
     float* tile = dW + (int64_t)(v0c + vl0) * D + d0;
-    tile_out<float>(acc, ACCUM ? tile : nullptr, tile, D, vc_act - vl0, D - d0);
+    tile_out<float>(acc, ACCUM ? tile : nullptr, tile, D, vc_act - vl0, D - d0, sc);
   };
   gemm_run<T>(lds, my_tile_count(tiles), even_slices<T>(tc_act), mk, epi);
 }
@@ -978,10 +1022,10 @@ inline size_t region(size_t bytes) { return (size_t)round_up((int64_t)bytes, 256
 
 bool sizes_ok(int64_t N, int64_t D, int64_t V, int dtype) {
   return N >= 1 && D >= 1 && V >= 1 && N <= kMaxDim && D <= kMaxHidden && V <= kMaxDim &&
-         (dtype == FLCE_F32 || dtype == FLCE_BF16);
+         (dtype == FLCE_F32 || dtype == FLCE_BF16 || dtype == FLCE_F16);
 }
 
-size_t elem_size(int dtype) { return dtype == FLCE_BF16 ? 2 : 4; }
+size_t elem_size(int dtype) { return dtype == FLCE_F32 ? 4 : 2; }
 
 // Workgroups resident at once: one 512-thread, ~150 KB-LDS workgroup per CU, 256 CUs.
 constexpr int kPersistentWGs = 256;
@@ -1017,7 +1061,7 @@ FwdLayout fwd_layout(int64_t N, int64_t V) {
 
 struct BwdLayout {
   int64_t tc, vc;  // chunk sizes (multiples of 256)
-  size_t e2, coef, lab, slab, dacc, total;
+  size_t e2, coef, lab, oscale, slab, dacc, total;
 };
 
 BwdLayout bwd_layout(int64_t N, int64_t D, int dtype, int64_t tc, int64_t vc) {
@@ -1031,10 +1075,12 @@ BwdLayout bwd_layout(int64_t N, int64_t D, int dtype, int64_t tc, int64_t vc) {
   off += region((size_t)N * 4);
   L.lab = off;
   off += region((size_t)N * 4);
+  L.oscale = off;
+  off += region(4);
   L.slab = off;
   off += region((size_t)tc * (size_t)vc * elem_size(dtype));
   L.dacc = off;
-  if (dtype == FLCE_BF16) off += region((size_t)tc * (size_t)D * 4);
+  if (dtype != FLCE_F32) off += region((size_t)tc * (size_t)D * 4);
   L.total = off;
   return L;
 }
@@ -1106,12 +1152,16 @@ flce_status backward_impl(const T* H, const T* W, const int64_t* y, const float*
   float* coef = reinterpret_cast<float*>(ws + L.coef);
   int* lab = reinterpret_cast<int*>(ws + L.lab);
   T* slab = reinterpret_cast<T*>(ws + L.slab);
-  float* dacc = dtype == FLCE_BF16 ? reinterpret_cast<float*>(ws + L.dacc) : nullptr;
+  float* dacc = dtype != FLCE_F32 ? reinterpret_cast<float*>(ws + L.dacc) : nullptr;
+  // fp16 slabs hold dz scaled by 2^14 / |g / N_valid| (dz itself is far below fp16's range
+  // at large N), undone by the dH and dW epilogues.
+  float* oscale = dtype == FLCE_F16 ? reinterpret_cast<float*>(ws + L.oscale) : nullptr;
+  const float fixed_scale = dtype == FLCE_F16 ? 16384.f : 0.f;
   const int ld_slab = (int)L.vc;
   const int n_td = (int)ceil_div(D, kTile);
   (void)hipGetLastError();
-  bwd_prep<<<dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, s>>>(lse, y, n_valid, grad, N, V, ignore_index, e2,
-                                                                  coef, lab);
+  bwd_prep<<<dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, s>>>(lse, y, n_valid, grad, N, V, ignore_index,
+                                                                  fixed_scale, e2, coef, lab, oscale);
   // Chunks of whole 256-row tiles, spread evenly: chunk i of n covers tiles
   // [i T / n, (i + 1) T / n) of the T tiles, never more than the workspace's chunk size.
   const int n_tc = (int)ceil_div(N, L.tc), n_vc = (int)ceil_div(V, L.vc);
@@ -1122,7 +1172,7 @@ flce_status backward_impl(const T* H, const T* W, const int64_t* y, const float*
     const int t1c = (int)((ci + 1) * t_tiles / n_tc * kTile);
     const int tc_act = (t1c < N ? t1c : N) - t0c;
     const int n_tt = (int)ceil_div(tc_act, kTile);
-    // fp32 accumulates dH in place; bf16 accumulates in the workspace and converts last.
+    // fp32 accumulates dH in place; 16-bit types accumulate in the workspace and convert last.
     float* acc_rows = dacc ? dacc : reinterpret_cast<float*>(dH) + (int64_t)t0c * D;
     for (int vi = 0; vi < n_vc; ++vi) {
       const int v0c = (int)(vi * v_tiles / n_vc * kTile);
@@ -1134,17 +1184,21 @@ flce_status backward_impl(const T* H, const T* W, const int64_t* y, const float*
       const dim3 gh(grid(n_tt * n_td)), gw(grid(n_vt * n_td)), blk(kThreads);
       const bool acc_dh = vi > 0, fin = dacc && vi == n_vc - 1;
       if (!acc_dh && !fin)
-        bwd_dh<T, false, false><<<gh, blk, 0, s>>>(slab, ld_slab, W, D, v0c, vc_act, t0c, tc_act, n_td, acc_rows, dH);
+        bwd_dh<T, false, false><<<gh, blk, 0, s>>>(slab, ld_slab, W, D, v0c, vc_act, t0c, tc_act, n_td, acc_rows, dH,
+                                                oscale);
       else if (acc_dh && !fin)
-        bwd_dh<T, true, false><<<gh, blk, 0, s>>>(slab, ld_slab, W, D, v0c, vc_act, t0c, tc_act, n_td, acc_rows, dH);
+        bwd_dh<T, true, false><<<gh, blk, 0, s>>>(slab, ld_slab, W, D, v0c, vc_act, t0c, tc_act, n_td, acc_rows, dH,
+                                                oscale);
       else if (!acc_dh && fin)
-        bwd_dh<T, false, true><<<gh, blk, 0, s>>>(slab, ld_slab, W, D, v0c, vc_act, t0c, tc_act, n_td, acc_rows, dH);
+        bwd_dh<T, false, true><<<gh, blk, 0, s>>>(slab, ld_slab, W, D, v0c, vc_act, t0c, tc_act, n_td, acc_rows, dH,
+                                                oscale);
       else
-        bwd_dh<T, true, true><<<gh, blk, 0, s>>>(slab, ld_slab, W, D, v0c, vc_act, t0c, tc_act, n_td, acc_rows, dH);
+        bwd_dh<T, true, true><<<gh, blk, 0, s>>>(slab, ld_slab, W, D, v0c, vc_act, t0c, tc_act, n_td, acc_rows, dH,
+                                                oscale);
       if (ci > 0)
-        bwd_dw<T, true><<<gw, blk, 0, s>>>(slab, ld_slab, H, D, t0c, tc_act, v0c, vc_act, n_td, dW);
+        bwd_dw<T, true><<<gw, blk, 0, s>>>(slab, ld_slab, H, D, t0c, tc_act, v0c, vc_act, n_td, dW, oscale);
       else
-        bwd_dw<T, false><<<gw, blk, 0, s>>>(slab, ld_slab, H, D, t0c, tc_act, v0c, vc_act, n_td, dW);
+        bwd_dw<T, false><<<gw, blk, 0, s>>>(slab, ld_slab, H, D, t0c, tc_act, v0c, vc_act, n_td, dW, oscale);
     }
   }
   return launched();
@@ -1176,7 +1230,7 @@ flce_status flce_forward(const void* H, const void* W, const int64_t* y, int64_t
                          int32_t* dev_status, void* workspace, size_t workspace_bytes, void* stream) {
   if (!sizes_ok(N, D, V, dtype) || !H || !W || !y || !loss || !lse || !n_valid || !dev_status || !workspace)
     return FLCE_ERR_INVALID_ARG;
-  const int64_t chunk = dtype == FLCE_BF16 ? 8 : 4;
+  const int64_t chunk = dtype == FLCE_F32 ? 4 : 8;
   if (D % chunk || !aligned(H, 16) || !aligned(W, 16) || !aligned(workspace, 16) || !aligned(y, 8) ||
       !aligned(lse, 4) || !aligned(loss, 4) || !aligned(n_valid, 4) || !aligned(dev_status, 4))
     return FLCE_ERR_ALIGN;
@@ -1185,6 +1239,9 @@ flce_status flce_forward(const void* H, const void* W, const int64_t* y, int64_t
   char* ws = reinterpret_cast<char*>(workspace);
   if (dtype == FLCE_BF16)
     return forward_impl<u16>(reinterpret_cast<const u16*>(H), reinterpret_cast<const u16*>(W), y, (int)N, (int)D,
+                             (int)V, ignore_index, loss, lse, n_valid, dev_status, ws, s);
+  if (dtype == FLCE_F16)
+    return forward_impl<h16>(reinterpret_cast<const h16*>(H), reinterpret_cast<const h16*>(W), y, (int)N, (int)D,
                              (int)V, ignore_index, loss, lse, n_valid, dev_status, ws, s);
   return forward_impl<float>(reinterpret_cast<const float*>(H), reinterpret_cast<const float*>(W), y, (int)N, (int)D,
                              (int)V, ignore_index, loss, lse, n_valid, dev_status, ws, s);
@@ -1195,7 +1252,7 @@ flce_status flce_backward(const void* H, const void* W, const int64_t* y, const 
                           void* dH, float* dW, void* workspace, size_t workspace_bytes, void* stream) {
   if (!sizes_ok(N, D, V, dtype) || !H || !W || !y || !lse || !n_valid || !dH || !dW || !workspace)
     return FLCE_ERR_INVALID_ARG;
-  const int64_t chunk = dtype == FLCE_BF16 ? 8 : 4;
+  const int64_t chunk = dtype == FLCE_F32 ? 4 : 8;
   if (D % chunk || !aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16) || !aligned(dW, 16) ||
       !aligned(workspace, 16) || !aligned(y, 8) || !aligned(lse, 4) || !aligned(n_valid, 4) ||
       (grad_loss && !aligned(grad_loss, 4)))
@@ -1208,6 +1265,10 @@ flce_status flce_backward(const void* H, const void* W, const int64_t* y, const 
   if (dtype == FLCE_BF16)
     return backward_impl<u16>(reinterpret_cast<const u16*>(H), reinterpret_cast<const u16*>(W), y, lse, n_valid,
                               grad_loss, (int)N, (int)D, (int)V, dtype, ignore_index, reinterpret_cast<u16*>(dH), dW,
+                              ws, L, s);
+  if (dtype == FLCE_F16)
+    return backward_impl<h16>(reinterpret_cast<const h16*>(H), reinterpret_cast<const h16*>(W), y, lse, n_valid,
+                              grad_loss, (int)N, (int)D, (int)V, dtype, ignore_index, reinterpret_cast<h16*>(dH), dW,
                               ws, L, s);
   return backward_impl<float>(reinterpret_cast<const float*>(H), reinterpret_cast<const float*>(W), y, lse, n_valid,
                               grad_loss, (int)N, (int)D, (int)V, dtype, ignore_index, reinterpret_cast<float*>(dH),

@@ -49,7 +49,7 @@ class Config:
     N: int  # tokens (batch x sequence)
     D: int  # hidden size
     V: int  # vocabulary size
-    dtype: str  # "f32" or "bf16"
+    dtype: str  # "f32", "bf16" or "f16"
     seed: int
     h_dist: str = "rms"  # "normal": N(0,1); "rms": N(0,1) rows scaled to unit RMS
     w_std: float = 0.02
@@ -69,8 +69,8 @@ class Config:
                 f"V={self.V}, {self.dtype}")
 
 
-# The five workloads.  The tiny fp32 case is the one the oracle finishes instantly;
-# the other four are shaped like the Llama-2, Mistral, Llama-3 and Qwen-2.5 heads.
+# The workloads.  The tiny fp32 case is the one the oracle finishes instantly; the next
+# four are shaped like the Llama-2, Mistral, Llama-3 and Qwen-2.5 heads.
 CONFIGS = {
     "tiny_f32": Config("tiny_f32", N=64, D=256, V=1024, dtype="f32", seed=1001,
                        h_dist="normal", ignore_frac=0.10, batch=1, seq=64),
@@ -82,6 +82,11 @@ CONFIGS = {
                      batch=4, seq=4096),
     "qwen25": Config("qwen25", N=8192, D=3584, V=152064, dtype="bf16", seed=1005,
                      ignore_frac=0.20, ignore_layout="tail", batch=1, seq=8192),
+    # fp16 variants of two of them (the pages name fp16 next to bf16)
+    "llama2_f16": Config("llama2_f16", N=4096, D=4096, V=32000, dtype="f16", seed=1006,
+                         batch=1, seq=4096),
+    "llama3_f16": Config("llama3_f16", N=16384, D=4096, V=128256, dtype="f16", seed=1007,
+                         batch=4, seq=4096),
 }
 
 
@@ -173,17 +178,25 @@ def _rne_bf16(x: np.ndarray) -> np.ndarray:
     return ((u + (0x7FFF + ((u >> 16) & 1))) >> 16).astype(np.uint16)
 
 
+def _rne_f16(x: np.ndarray) -> np.ndarray:
+    """fp32 -> IEEE fp16, round to nearest even (numpy's conversion), as uint16 bits."""
+    return x.astype(np.float16).view(np.uint16)
+
+
+_ROUND16 = {"bf16": _rne_bf16, "f16": _rne_f16}
+
+
 def _normal_rows(rows: int, cols: int, seed: int, tensor: int, threads: int, finish,
                  dtype: str) -> np.ndarray:
-    """[rows, cols] of finish(standard normals) rounded to fp32, then (dtype "bf16") to
-    bf16 bit patterns; block b (4096 rows) draws from its own stream."""
+    """[rows, cols] of finish(standard normals) rounded to fp32, then (dtype "bf16" or
+    "f16") to 16-bit patterns; block b (4096 rows) draws from its own stream."""
     out = np.empty((rows, cols), dtype=np.float32 if dtype == "f32" else np.uint16)
     nblk = (rows + _BLOCK_ROWS - 1) // _BLOCK_ROWS
 
     def fill(b: int) -> None:
         r0, r1 = b * _BLOCK_ROWS, min(rows, (b + 1) * _BLOCK_ROWS)
         blk = finish(_gaussian_block(seed, tensor, b, r1 - r0, cols)).astype(np.float32)
-        out[r0:r1] = blk if dtype == "f32" else _rne_bf16(blk)
+        out[r0:r1] = blk if dtype == "f32" else _ROUND16[dtype](blk)
 
     if nblk == 1 or threads <= 1:
         for b in range(nblk):
@@ -204,7 +217,7 @@ def _unit_rms(x: np.ndarray) -> np.ndarray:
 @dataclass
 class Inputs:
     """Generated inputs.  ``H`` and ``W`` are fp32 tensors for f32 workloads and int16
-    bf16 bit patterns for bf16 workloads; ``y`` is int64 with IGNORE_INDEX rows."""
+    bit patterns for bf16 / f16 workloads; ``y`` is int64 with IGNORE_INDEX rows."""
 
     cfg: Config
     H: torch.Tensor
@@ -214,7 +227,7 @@ class Inputs:
 
     @property
     def torch_dtype(self) -> torch.dtype:
-        return torch.float32 if self.cfg.dtype == "f32" else torch.bfloat16
+        return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[self.cfg.dtype]
 
     def h64(self) -> np.ndarray:
         return self._widen(self.H)
@@ -228,6 +241,8 @@ class Inputs:
     def _widen(self, t: torch.Tensor) -> np.ndarray:
         if self.cfg.dtype == "f32":
             return t.numpy().astype(np.float64)
+        if self.cfg.dtype == "f16":
+            return t.numpy().view(np.float16).astype(np.float64)
         return bf16_bits_to_f64(t.numpy())
 
     def device_tensors(self, device) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
@@ -235,7 +250,7 @@ class Inputs:
         if self.cfg.dtype == "f32":
             H, W = self.H, self.W
         else:
-            H, W = self.H.view(torch.bfloat16), self.W.view(torch.bfloat16)
+            H, W = self.H.view(self.torch_dtype), self.W.view(self.torch_dtype)
         return (H.to(device).contiguous(), W.to(device).contiguous(),
                 self.y.to(device).contiguous())
 
@@ -289,7 +304,7 @@ def generate(cfg: Config, threads: int = 8) -> Inputs:
             raise ValueError(cfg.ignore_layout)
         y[idx] = IGNORE_INDEX
 
-    if cfg.dtype == "bf16":
+    if cfg.dtype in ("bf16", "f16"):
         Ht, Wt = torch.from_numpy(H.view(np.int16)), torch.from_numpy(W.view(np.int16))
     elif cfg.dtype == "f32":
         Ht, Wt = torch.from_numpy(H), torch.from_numpy(W)
@@ -317,6 +332,9 @@ def with_weights_scaled(inp: Inputs, factor: float) -> Inputs:
     element type) -- large-logit tests."""
     if inp.cfg.dtype == "f32":
         W = torch.from_numpy(inp.W.numpy() * np.float32(factor))
+    elif inp.cfg.dtype == "f16":
+        w32 = inp.W.numpy().view(np.float16).astype(np.float32)
+        W = torch.from_numpy(_rne_f16(w32 * np.float32(factor)).view(np.int16))
     else:
         w32 = (inp.W.numpy().view(np.uint16).astype(np.uint32) << 16).view(np.float32)
         W = torch.from_numpy(_rne_bf16(w32 * np.float32(factor)).view(np.int16))

@@ -5,9 +5,13 @@ import numpy as np
 import torch
 
 # relative tolerances: (loss, lse max, dH / dW Frobenius)
+# fp16: inputs are the same on both sides; logits accumulate in fp32 (relative error
+# ~1e-6); the gradient carries fp16 rounding of the scaled dz (2^-11 relative) and of dH
+# (2^-12), about 7e-4 together, bounded here at 3e-3.
 TOL = {
     "f32": dict(loss=1e-5, lse=1e-5, grad=1e-5),
     "bf16": dict(loss=2e-3, lse=2e-3, grad=1e-2),
+    "f16": dict(loss=1e-4, lse=1e-4, grad=3e-3),
 }
 
 

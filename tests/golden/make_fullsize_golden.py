@@ -1,5 +1,5 @@
-"""Write tests/golden/fullsize_<workload>.npz: fp64 oracle values for the four
-full-size bf16 workloads (Llama-2, Mistral, Llama-3 and Qwen-2.5 shaped heads).
+"""Write tests/golden/fullsize_<workload>.npz: fp64 oracle values for the full-size
+workloads (Llama-2, Mistral, Llama-3 and Qwen-2.5 shaped heads in bf16, Llama-2 in fp16).
 
 Only the oracle and the seeded input generator are used.  Stored per workload:
   digest         fingerprint of the exact input bytes (checked before comparing)
@@ -22,7 +22,7 @@ sys.path.insert(0, os.path.dirname(os.path.dirname(HERE)))
 import oracle  # noqa: E402
 from linear_cross_entropy_lm_amd import inputs as I  # noqa: E402
 
-WORKLOADS = ["llama2", "mistral", "llama3", "qwen25"]
+WORKLOADS = ["llama2", "mistral", "llama3", "qwen25", "llama2_f16"]
 
 
 def pick_rows(y: np.ndarray, rng) -> np.ndarray:

@@ -49,19 +49,20 @@ def _fwd_bytes(N, V):
     return _r(splits * N * 8) + _r(N * 4) + _r(ntn * 8) + 2 * _r(ntn * 4)
 
 
-def _bwd_bytes(N, D, esize, tc, vc, bf16):
-    return 3 * _r(N * 4) + _r(tc * vc * esize) + (_r(tc * D * 4) if bf16 else 0)
+def _bwd_bytes(N, D, esize, tc, vc, half):
+    return 3 * _r(N * 4) + _r(4) + _r(tc * vc * esize) + (_r(tc * D * 4) if half else 0)
 
 
 @pytest.mark.parametrize("N,D,V,dt", [(64, 256, 1024, 0), (4096, 4096, 32000, 1), (8192, 4096, 32768, 1),
                                       (16384, 4096, 128256, 1), (8192, 3584, 152064, 1), (1, 8, 1, 1),
-                                      (700, 384, 3000, 0)])
+                                      (700, 384, 3000, 0), (4096, 4096, 32000, 2), (16384, 4096, 128256, 2),
+                                      (1, 8, 1, 2)])
 def test_workspace_formula(B, N, D, V, dt):
-    esize = 2 if dt == 1 else 4
+    esize = 4 if dt == 0 else 2
     tc, vc = _r(min(N, 4096)), _r(min(V, 8192))
-    while vc > 4096 and _bwd_bytes(N, D, esize, tc, vc, dt == 1) > 0.05 * 2 * N * V:
+    while vc > 4096 and _bwd_bytes(N, D, esize, tc, vc, dt != 0) > 0.05 * 2 * N * V:
         vc -= 256
-    expect = max(_fwd_bytes(N, V), _bwd_bytes(N, D, esize, tc, vc, dt == 1))
+    expect = max(_fwd_bytes(N, V), _bwd_bytes(N, D, esize, tc, vc, dt != 0))
     assert B.flce_workspace_bytes(N, D, V, dt) == expect
     assert B.flce_backward_chunks(N, D, V, dt, expect) == (tc, vc)
 
@@ -125,6 +126,7 @@ def test_forward_argument_errors(B):
     assert _fwd(B, dt=3) == B.FLCE_ERR_INVALID_ARG
     assert _fwd(B, H=A16 + 8) == B.FLCE_ERR_ALIGN
     assert _fwd(B, D=12) == B.FLCE_ERR_ALIGN            # bf16 needs D % 8 == 0
+    assert _fwd(B, D=12, dt=2) == B.FLCE_ERR_ALIGN      # and so does fp16
     assert _fwd(B, y=A16 + 4) == B.FLCE_ERR_ALIGN
     assert _fwd(B, wsb=16) == B.FLCE_ERR_WORKSPACE
 

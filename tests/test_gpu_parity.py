@@ -2,7 +2,8 @@
 on seeded inputs that span several 256-wide tiles and ragged tails, plus edge cases.
 
 Tolerances (relative): fp32 inputs -- loss 1e-5, lse 1e-5, dH/dW Frobenius 1e-5;
-bf16 inputs with fp32 accumulation -- loss 2e-3, lse 2e-3, dH/dW Frobenius 1e-2.
+bf16 inputs with fp32 accumulation -- loss 2e-3, lse 2e-3, dH/dW Frobenius 1e-2;
+fp16 inputs -- loss 1e-4, lse 1e-4, dH/dW Frobenius 3e-3 (derivation in flce_run.TOL).
 """
 import numpy as np
 import pytest
@@ -38,6 +39,9 @@ CASES = [
     ("raggedD_f32", I.case(257, 260, 777, "f32", seed=14)),
     ("zipf_bf16", I.case(640, 256, 4099, "bf16", seed=15, label_dist="zipf")),
     ("tail_ignore_bf16", I.case(512, 384, 1536, "bf16", seed=16, ignore_frac=0.2, ignore_layout="tail")),
+    ("ragged_f16", I.case(300, 512, 1031, "f16", seed=17)),
+    ("raggedD_f16", I.case(513, 264, 2500, "f16", seed=18, ignore_frac=0.2)),
+    ("zipf_f16", I.case(640, 256, 4099, "f16", seed=19, label_dist="zipf")),
 ]
 
 
@@ -52,7 +56,10 @@ def test_parity_small(name, cfg):
     _say("errors", err)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+_TORCH = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_parity_multi_chunk_backward(dtype):
     """A workspace that forces 256-token x 512-vocab chunks: dH accumulates over vocab
     chunks and dW over token chunks."""
@@ -60,7 +67,7 @@ def test_parity_multi_chunk_backward(dtype):
     cfg = I.case(700, 384, 3000, dtype, seed=21)
     _say("case", cfg.describe())
     inp = I.generate(cfg)
-    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tdt = _TORCH[dtype]
     full = B.flce_workspace_bytes(cfg.N, cfg.D, cfg.V, tdt)
     ws = None
     for cand in range(full, 0, -4096):
@@ -109,9 +116,10 @@ def test_single_valid_row():
     assert np.all(got["dH"][np.arange(300) != 137] == 0.0)
 
 
-def test_large_logits_stable():
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_large_logits_stable(dtype):
     """W x 100: logits of a few hundred; the online log-sum-exp must not overflow."""
-    cfg = I.case(300, 256, 1100, "bf16", seed=43)
+    cfg = I.case(300, 256, 1100, dtype, seed=43)
     inp = I.with_weights_scaled(I.generate(cfg), 100.0)
     got = run_gpu(inp)
     ref = _oracle(inp)
@@ -132,15 +140,18 @@ def test_invalid_label_sets_status_and_is_ignored():
     compare(got, ref, "bf16")
 
 
-def test_custom_ignore_index_and_upstream_grad():
-    cfg = I.case(400, 256, 900, "f32", seed=45, ignore_frac=0.0)
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_custom_ignore_index_and_upstream_grad(dtype):
+    """A negative upstream gradient (the sign path of the dz scaling) and a label value
+    used as ignore_index."""
+    cfg = I.case(400, 256, 900, dtype, seed=45, ignore_frac=0.0)
     inp0 = I.generate(cfg)
     y = inp0.y.clone()
     y[::7] = 5
     inp = I.with_labels(inp0, y)
     got = run_gpu(inp, g=-2.5, ignore_index=5)
     ref = _oracle(inp, g=-2.5, ignore_index=5)
-    compare(got, ref, "f32")
+    compare(got, ref, dtype)
 
 
 def test_bitwise_deterministic():
