@@ -1,9 +1,15 @@
 """Benchmark: fused lm_head projection + cross-entropy, forward + backward, on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload llama3] [--cpu-rows R | --no-cpu-baseline]
+    python bench.py --path ce [--workload ce_llama3] ...
 
 One step = flce_forward + flce_backward over one batch of synthetic input already
 resident in HBM (loss, lse, dH, dW all produced).  Prints one JSON line.
+
+--path ce measures the cross-entropy over materialised logits instead (include/flce_ce.h):
+one step = flce_ce_forward + flce_ce_backward over bf16 logits [16384, 128256] in HBM
+(loss, lse, dZ into a separate buffer); its roofline is the backward kernel (ce_rows_bwd)
+against the HBM peak (8 TB/s), 2 V es + 12 bytes per row (ce_row_bytes).
 
 value        tokens per second (N / mean step time over the timed steps), the whole job
              on one GPU; per-step median/min/max from events around each step
@@ -27,28 +33,42 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "fused linear-CE fwd+bwd tokens/s at N=16384,D=4096,V=128256; % bf16 MFMA peak"
+METRIC_CE = "cross-entropy over materialised logits fwd+bwd tokens/s at N=16384,V=128256; % HBM peak"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_tiles_llama3_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "linear_cross_entropy_lm_amd", "csrc", "flce.hip")
+CSRC = os.path.join(ROOT, "linear_cross_entropy_lm_amd", "csrc")
+# path -> (dominant kernel, workload, traffic record, kernel source)
+PATHS = {
+    "fused": ("fwd_tiles", "llama3", os.path.join(ROOT, "profiles", "fwd_tiles_llama3_traffic.json"),
+              os.path.join(CSRC, "flce.hip")),
+    "ce": ("ce_rows_bwd", "ce_llama3", os.path.join(ROOT, "profiles", "ce_rows_bwd_ce_llama3_traffic.json"),
+           os.path.join(CSRC, "ce_logits.hip")),
+}
 
 
-def source_digest() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def source_digest(path: str = "fused") -> str:
+    with open(PATHS[path][3], "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def load_traffic():
-    """HBM bytes per fwd_tiles launch from the committed counter summary, or None when
-    absent or taken on a different kernel source."""
+def load_traffic(path: str = "fused"):
+    """HBM bytes per launch of the path's dominant kernel from the committed counter
+    summary, or None when absent or taken on a different kernel source."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(PATHS[path][2]) as f:
             t = json.load(f)
     except OSError:
         return None
-    if t.get("source_digest") != source_digest():
+    if t.get("source_digest") != source_digest(path):
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def ce_row_bytes(V: int, es: int) -> tuple[int, int]:
+    """Algorithmic HBM bytes per row of the cross-entropy over logits: forward reads the
+    row (V es) and its label (8) and writes lse (4), the row's loss term (8) and flag (4);
+    backward reads the row, label and lse and writes the row of dZ (V es)."""
+    return V * es + 24, 2 * V * es + 12
 
 
 def _counter_per_dispatch(csv_dir: str, counter: str, kernel_prefix: str):
@@ -67,23 +87,24 @@ def _counter_per_dispatch(csv_dir: str, counter: str, kernel_prefix: str):
     return sum(vals.values()) / len(vals), len(vals)
 
 
-def summarize_counters(root: str, copy_bytes: int) -> dict:
-    """Write the fwd_tiles HBM traffic record from four rocprofv3 --pmc runs under root:
-    F (FETCH_SIZE) and W (WRITE_SIZE) of `bench.py --steps 1 --warmup 0 --no-cpu-baseline`,
-    FC and WC of `bench.py --calibrate-copy copy_bytes`.  Each counter is scaled by what it
-    reads for the copy (copy_bytes read and copy_bytes written)."""
-    fetch, n_f = _counter_per_dispatch(os.path.join(root, "F"), "FETCH_SIZE", "fwd_tiles")
-    write, n_w = _counter_per_dispatch(os.path.join(root, "W"), "WRITE_SIZE", "fwd_tiles")
+def summarize_counters(root: str, copy_bytes: int, path: str = "fused") -> dict:
+    """Write the dominant kernel's HBM traffic record from four rocprofv3 --pmc runs under
+    root: F (FETCH_SIZE) and W (WRITE_SIZE) of `bench.py [--path ce] --steps 1 --warmup 0
+    --no-cpu-baseline`, FC and WC of `bench.py --calibrate-copy copy_bytes`.  Each counter
+    is scaled by what it reads for the copy (copy_bytes read and copy_bytes written)."""
+    kernel, workload, traffic_file, _ = PATHS[path]
+    fetch, n_f = _counter_per_dispatch(os.path.join(root, "F"), "FETCH_SIZE", kernel)
+    write, n_w = _counter_per_dispatch(os.path.join(root, "W"), "WRITE_SIZE", kernel)
     cf, _ = _counter_per_dispatch(os.path.join(root, "FC"), "FETCH_SIZE", "copyBuffer")
     cw, _ = _counter_per_dispatch(os.path.join(root, "WC"), "WRITE_SIZE", "copyBuffer")
     f_factor = copy_bytes / (cf * 1024.0)
     w_factor = copy_bytes / (cw * 1024.0)
-    rec = {"kernel": "fwd_tiles", "workload": "llama3", "source_digest": source_digest(),
+    rec = {"kernel": kernel, "workload": workload, "source_digest": source_digest(path),
            "fetch_kib_per_launch": fetch, "write_kib_per_launch": write, "launches": [n_f, n_w],
            "copy_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
            "fetch_factor": f_factor, "write_factor": w_factor,
            "hbm_bytes_per_launch": fetch * 1024.0 * f_factor + write * 1024.0 * w_factor}
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(traffic_file, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
     return rec
@@ -110,44 +131,37 @@ def cpu_baseline(inp, rows: int) -> dict:
             "seconds": dt, "fp64_gflops": 6.0 * rows * inp.cfg.V * inp.cfg.D / dt / 1e9}
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="llama3")
-    ap.add_argument("--cpu-rows", type=int, default=1024)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
-                    help="only run one device-to-device copy of BYTES bytes (counter calibration)")
-    ap.add_argument("--summarize-counters", metavar="DIR",
-                    help="only write the fwd_tiles traffic record from rocprofv3 counter runs under DIR "
-                         "(subdirectories F, W, FC, WC); no GPU needed")
-    ap.add_argument("--copy-bytes", type=int, default=1 << 30)
-    args = ap.parse_args()
-    if args.summarize_counters:
-        print(json.dumps(summarize_counters(args.summarize_counters, args.copy_bytes)), flush=True)
-        return 0
-    if args.calibrate_copy:
-        import torch
-        src = torch.ones(args.calibrate_copy // 4, dtype=torch.float32, device="cuda:0")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copied_bytes": args.calibrate_copy}), flush=True)
-        return 0
-    if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU (asked for {args.gpus}); the multi-GPU "
-              "sharding of the path is described, not built.", file=sys.stderr)
-        return 2
+def cpu_baseline_ce(inp, rows: int) -> dict:
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    Z = inp.z64(np.arange(rows))
+    y = inp.y64()[:rows]
+    t0 = time.perf_counter()
+    oracle.ce_from_logits(Z, y)
+    dt = time.perf_counter() - t0
+    return {"value": rows / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {rows} of {inp.cfg.N} logit rows, full V={inp.cfg.V}: fp64 loss, lse and dZ "
+                      f"in {dt:.1f} s", "seconds": dt}
 
+
+def _common(args, metric, value, ms, dtype, data, config):
+    return {"metric": metric, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": dtype, "data": data, "config": config}
+
+
+def run_fused(args) -> dict:
     import torch
     from linear_cross_entropy_lm_amd import binding as B
     from linear_cross_entropy_lm_amd import inputs as I
     from linear_cross_entropy_lm_amd.scratch import scratch_fraction
 
-    cfg = I.CONFIGS[args.workload]
+    cfg = I.CONFIGS[args.workload or "llama3"]
     inp = I.generate(cfg)
     dev = "cuda:0"
     H, W, y = inp.device_tensors(dev)
@@ -172,10 +186,109 @@ def main() -> int:
         if ev is not None:
             ev[2].record(stream)
 
+    ms, fwd_ms, step_ms, peak_delta = _time_steps(args, step, stream)
+    if int(st.item()) != 0:
+        raise RuntimeError("dev_status reports invalid labels")
+
+    flop_step = 8.0 * N * V * D
+    fwd_flop = 2.0 * N * V * D
+    achieved = fwd_flop / (fwd_ms * 1e-3) / 1e12
+    out = _common(args, METRIC, N / (ms * 1e-3), ms, cfg.dtype,
+                  "synthetic: seeded Gaussian H with unit-RMS rows, W ~ N(0, 0.02^2), uniform labels, "
+                  f"{cfg.n_ignored} ignore_index rows",
+                  {"workload": f"{cfg.name}-shaped lm_head + cross-entropy, fwd+bwd", "N": N, "D": D,
+                   "V": V, "batch": cfg.batch, "seq_len": cfg.seq, "parallelism": "single GPU"})
+    out.update({
+        "mfma_peak_frac": flop_step / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+        "useful_flop_frac": 0.75 * flop_step / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+        "fwd_ms": fwd_ms,
+        "bwd_ms": ms - fwd_ms,
+        "step_ms_median": step_ms[len(step_ms) // 2],
+        "step_ms_min": step_ms[0],
+        "step_ms_max": step_ms[-1],
+        "scratch_bytes": ws_bytes,
+        "torch_peak_alloc_delta_bytes": int(peak_delta),
+        "scratch_frac_of_unfused_logits": scratch_fraction(ws_bytes, N, V),
+        "loss": float(loss.item()),
+        "roofline": {"kernel": "fwd_tiles", "bound": "mfma", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": load_traffic("fused")},
+        "cpu_baseline": None,
+    })
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows or 1024)
+    return out
+
+
+def run_ce(args) -> dict:
+    import torch
+    from linear_cross_entropy_lm_amd import binding as B
+    from linear_cross_entropy_lm_amd import inputs as I
+
+    cfg = I.LOGIT_CONFIGS[args.workload or "ce_llama3"]
+    inp = I.generate_logits(cfg)
+    dev = "cuda:0"
+    Z, y = inp.device_tensors(dev)
+    N, V = cfg.N, cfg.V
+    es = Z.element_size()
+    ws = torch.empty(B.flce_ce_workspace_bytes(N), dtype=torch.uint8, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    nv = torch.empty(1, dtype=torch.int32, device=dev)
+    st = torch.empty(1, dtype=torch.int32, device=dev)
+    dZ = torch.empty_like(Z)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        B.flce_ce_forward(Z, y, loss, lse, nv, st, ws, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        B.flce_ce_backward(Z, y, lse, nv, None, dZ, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    ms, fwd_ms, step_ms, peak_delta = _time_steps(args, step, stream)
+    if int(st.item()) != 0:
+        raise RuntimeError("dev_status reports invalid labels")
+    bwd_ms = ms - fwd_ms
+    fwd_row, bwd_row = ce_row_bytes(V, es)
+    achieved = bwd_row * N / (bwd_ms * 1e-3) / 1e9
+    step_bytes = (fwd_row + bwd_row) * N
+    out = _common(args, METRIC_CE, N / (ms * 1e-3), ms, cfg.dtype,
+                  f"synthetic: seeded logits N(0, {cfg.z_std}^2), uniform labels, {cfg.n_ignored} ignore_index rows",
+                  {"workload": f"{cfg.name}: cross-entropy over materialised logits, fwd+bwd", "N": N, "V": V,
+                   "row_pitch": cfg.pitch, "parallelism": "single GPU"})
+    out.update({
+        "hbm_peak_frac": step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "fwd_ms": fwd_ms,
+        "bwd_ms": bwd_ms,
+        "fwd_gbs": fwd_row * N / (fwd_ms * 1e-3) / 1e9,
+        "step_ms_median": step_ms[len(step_ms) // 2],
+        "step_ms_min": step_ms[0],
+        "step_ms_max": step_ms[-1],
+        "torch_peak_alloc_delta_bytes": int(peak_delta),
+        "loss": float(loss.item()),
+        "roofline": {"kernel": "ce_rows_bwd", "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": load_traffic("ce")},
+        "cpu_baseline": None,
+    })
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_ce(inp, args.cpu_rows or 8192)
+    return out
+
+
+def _time_steps(args, step, stream):
+    """W warmup steps, one step under torch's allocator peak tracking (the library
+    allocates nothing, so the peak stays at what is already held), then K timed steps
+    with events around each step and around the whole run.  Returns the mean step ms, the
+    mean ms of the first half of each step (the forward), the sorted per-step ms and the
+    allocator peak delta."""
+    import torch
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # the library allocates nothing: torch's peak over one step stays at what is already held
     held = torch.cuda.memory_allocated()
     torch.cuda.reset_peak_memory_stats()
     step()
@@ -192,47 +305,45 @@ def main() -> int:
     ms = start.elapsed_time(end) / args.steps
     fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     step_ms = sorted(e[0].elapsed_time(e[2]) for e in evs)
-    if int(st.item()) != 0:
-        raise RuntimeError("dev_status reports invalid labels")
+    return ms, fwd_ms, step_ms, peak_delta
 
-    flop_step = 8.0 * N * V * D
-    fwd_flop = 2.0 * N * V * D
-    achieved = fwd_flop / (fwd_ms * 1e-3) / 1e12
-    traffic = load_traffic()
-    out = {
-        "metric": METRIC,
-        "value": N / (ms * 1e-3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": cfg.dtype,
-        "data": "synthetic: seeded Gaussian H with unit-RMS rows, W ~ N(0, 0.02^2), uniform labels, "
-                f"{cfg.n_ignored} ignore_index rows",
-        "config": {"workload": f"{cfg.name}-shaped lm_head + cross-entropy, fwd+bwd", "N": N, "D": D,
-                   "V": V, "batch": cfg.batch, "seq_len": cfg.seq, "parallelism": "single GPU"},
-        "mfma_peak_frac": flop_step / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
-        "useful_flop_frac": 0.75 * flop_step / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
-        "fwd_ms": fwd_ms,
-        "bwd_ms": ms - fwd_ms,
-        "step_ms_median": step_ms[len(step_ms) // 2],
-        "step_ms_min": step_ms[0],
-        "step_ms_max": step_ms[-1],
-        "scratch_bytes": ws_bytes,
-        "torch_peak_alloc_delta_bytes": int(peak_delta),
-        "scratch_frac_of_unfused_logits": scratch_fraction(ws_bytes, N, V),
-        "loss": float(loss.item()),
-        "roofline": {"kernel": "fwd_tiles", "bound": "mfma", "achieved": achieved,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": traffic},
-        "cpu_baseline": None,
-    }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows)
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--path", choices=sorted(PATHS), default="fused",
+                    help="fused: lm_head projection + cross-entropy (default); ce: cross-entropy over "
+                         "materialised logits")
+    ap.add_argument("--workload", default=None, help="default llama3 (fused) or ce_llama3 (ce)")
+    ap.add_argument("--cpu-rows", type=int, default=None,
+                    help="rows of the oracle sample (default 1024 fused, 8192 ce: 10-20 s of CPU work)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run one device-to-device copy of BYTES bytes (counter calibration)")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="only write the path's traffic record from rocprofv3 counter runs under DIR "
+                         "(subdirectories F, W, FC, WC); no GPU needed")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    args = ap.parse_args()
+    if args.summarize_counters:
+        print(json.dumps(summarize_counters(args.summarize_counters, args.copy_bytes, args.path)), flush=True)
+        return 0
+    if args.calibrate_copy:
+        import torch
+        src = torch.ones(args.calibrate_copy // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copied_bytes": args.calibrate_copy}), flush=True)
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU (asked for {args.gpus}); the multi-GPU "
+              "sharding of the path is described, not built.", file=sys.stderr)
+        return 2
+    out = run_ce(args) if args.path == "ce" else run_fused(args)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -1,4 +1,4 @@
-"""ctypes binding of libflce.so (include/flce.h).  Argument marshalling only: every step
+"""ctypes binding of libflce.so (include/flce.h, include/flce_ce.h).  Argument marshalling only: every step
 of the computation runs in the library's HIP kernels; torch provides device memory and
 the current stream.
 
@@ -18,7 +18,7 @@ FLCE_OK, FLCE_ERR_INVALID_ARG, FLCE_ERR_ALIGN, FLCE_ERR_WORKSPACE, FLCE_ERR_HIP 
 FLCE_F32, FLCE_BF16, FLCE_F16 = 0, 1, 2
 IGNORE_INDEX = -100
 
-# symbol -> (restype, argtypes), in the order of include/flce.h
+# symbol -> (restype, argtypes), in the order of include/flce.h then include/flce_ce.h
 _P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
 SIGNATURES = {
     "flce_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I32]),
@@ -26,6 +26,9 @@ SIGNATURES = {
     "flce_forward": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I32, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
     "flce_backward": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I64, _P, _P, _P, _SZ, _P]),
     "flce_status_string": (ctypes.c_char_p, [_I32]),
+    "flce_ce_workspace_bytes": (_SZ, [_I64]),
+    "flce_ce_forward": (_I32, [_P, _I64, _P, _I64, _I64, _I32, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
+    "flce_ce_backward": (_I32, [_P, _I64, _P, _P, _P, _P, _I64, _I64, _I32, _I64, _P, _I64, _P]),
 }
 
 
@@ -137,6 +140,59 @@ def flce_backward(H, W, y, lse, n_valid, grad_loss, dH, dW, workspace, ignore_in
                            _ptr(workspace), workspace.numel(), _stream(stream))
     if st != FLCE_OK:
         raise FlceError(st, "flce_backward")
+
+
+# --- cross-entropy over materialised logits (include/flce_ce.h) ----------------------
+
+
+def _check_rows(t: torch.Tensor, name: str) -> int:
+    """A 2-D device tensor whose rows are contiguous (row pitch t.stride(0) >= t.shape[1]);
+    returns the pitch."""
+    if not t.is_cuda or t.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D device tensor")
+    if t.stride(1) != 1 or t.stride(0) < t.shape[1]:
+        raise ValueError(f"{name} must have contiguous rows")
+    return t.stride(0)
+
+
+def flce_ce_workspace_bytes(N: int) -> int:
+    return int(lib.flce_ce_workspace_bytes(int(N)))
+
+
+def flce_ce_forward(Z, y, loss, lse, n_valid, dev_status, workspace, ignore_index=IGNORE_INDEX,
+                    stream=None) -> None:
+    """Mean cross-entropy of logits Z [N, V] (row pitch Z.stride(0)) against y."""
+    ld = _check_rows(Z, "Z")
+    N, V = Z.shape
+    _check(y, "y", torch.int64, (N,))
+    _check(loss, "loss", torch.float32, (1,))
+    _check(lse, "lse", torch.float32, (N,))
+    _check(n_valid, "n_valid", torch.int32, (1,))
+    _check(dev_status, "dev_status", torch.int32, (1,))
+    _check(workspace, "workspace", torch.uint8)
+    st = lib.flce_ce_forward(_ptr(Z), ld, _ptr(y), N, V, dtype_code(Z.dtype), ignore_index, _ptr(loss),
+                             _ptr(lse), _ptr(n_valid), _ptr(dev_status), _ptr(workspace), workspace.numel(),
+                             _stream(stream))
+    if st != FLCE_OK:
+        raise FlceError(st, "flce_ce_forward")
+
+
+def flce_ce_backward(Z, y, lse, n_valid, grad_loss, dZ, ignore_index=IGNORE_INDEX, stream=None) -> None:
+    """dZ = (softmax(Z) - onehot(y)) * g / N_valid; dZ may be Z itself."""
+    ld = _check_rows(Z, "Z")
+    ldo = _check_rows(dZ, "dZ")
+    N, V = Z.shape
+    if tuple(dZ.shape) != (N, V) or dZ.dtype != Z.dtype:
+        raise ValueError("dZ must match Z's shape and dtype")
+    _check(y, "y", torch.int64, (N,))
+    _check(lse, "lse", torch.float32, (N,))
+    _check(n_valid, "n_valid", torch.int32, (1,))
+    if grad_loss is not None:
+        _check(grad_loss, "grad_loss", torch.float32, (1,))
+    st = lib.flce_ce_backward(_ptr(Z), ld, _ptr(y), _ptr(lse), _ptr(n_valid), _ptr(grad_loss), N, V,
+                              dtype_code(Z.dtype), ignore_index, _ptr(dZ), ldo, _stream(stream))
+    if st != FLCE_OK:
+        raise FlceError(st, "flce_ce_backward")
 
 
 class FusedLinearCrossEntropy(torch.autograd.Function):

@@ -11,7 +11,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "flce.hip")
+SRCS = [os.path.join(PKG, "csrc", "flce.hip"), os.path.join(PKG, "csrc", "ce_logits.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libflce.so")
 
@@ -34,9 +34,10 @@ def hipcc() -> str:
 
 
 def build_library(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
-    """Compile csrc/flce.hip into libflce.so (always recompiles)."""
+    """Compile csrc/*.hip (the fused path and the standalone cross-entropy over logits)
+    into libflce.so (always recompiles)."""
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), "-I", INCLUDE, SRC, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), "-I", INCLUDE, *SRCS, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -187,14 +187,14 @@ _ROUND16 = {"bf16": _rne_bf16, "f16": _rne_f16}
 
 
 def _normal_rows(rows: int, cols: int, seed: int, tensor: int, threads: int, finish,
-                 dtype: str) -> np.ndarray:
+                 dtype: str, block_rows: int = _BLOCK_ROWS) -> np.ndarray:
     """[rows, cols] of finish(standard normals) rounded to fp32, then (dtype "bf16" or
-    "f16") to 16-bit patterns; block b (4096 rows) draws from its own stream."""
+    "f16") to 16-bit patterns; block b (block_rows rows) draws from its own stream."""
     out = np.empty((rows, cols), dtype=np.float32 if dtype == "f32" else np.uint16)
-    nblk = (rows + _BLOCK_ROWS - 1) // _BLOCK_ROWS
+    nblk = (rows + block_rows - 1) // block_rows
 
     def fill(b: int) -> None:
-        r0, r1 = b * _BLOCK_ROWS, min(rows, (b + 1) * _BLOCK_ROWS)
+        r0, r1 = b * block_rows, min(rows, (b + 1) * block_rows)
         blk = finish(_gaussian_block(seed, tensor, b, r1 - r0, cols)).astype(np.float32)
         out[r0:r1] = blk if dtype == "f32" else _ROUND16[dtype](blk)
 
@@ -265,19 +265,9 @@ class Inputs:
         return self._digest
 
 
-def generate(cfg: Config, threads: int = 8) -> Inputs:
-    """Draw H, W, labels and the ignore mask (in that order) for ``cfg``.  Every step is
-    integer arithmetic or correctly rounded floating point, so the bytes are the same on
-    any host."""
-    N, D, V = cfg.N, cfg.D, cfg.V
-    if cfg.h_dist == "rms":
-        H = _normal_rows(N, D, cfg.seed, _TENSOR_H, threads, _unit_rms, cfg.dtype)
-    elif cfg.h_dist == "normal":
-        H = _normal_rows(N, D, cfg.seed, _TENSOR_H, threads, lambda z: z, cfg.dtype)
-    else:
-        raise ValueError(cfg.h_dist)
-    W = _normal_rows(V, D, cfg.seed, _TENSOR_W, threads, lambda z: z * cfg.w_std, cfg.dtype)
-
+def _draw_labels(cfg, N: int, V: int) -> np.ndarray:
+    """Labels then the ignore mask for a workload (uniform or Zipf over a random vocabulary
+    permutation; ignored rows at random positions or as a contiguous tail)."""
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg.seed, _TENSOR_LABELS, 0])))
     if cfg.label_dist == "uniform":
         y = rng.integers(0, V, size=N, dtype=np.int64)
@@ -304,6 +294,24 @@ def generate(cfg: Config, threads: int = 8) -> Inputs:
             raise ValueError(cfg.ignore_layout)
         y[idx] = IGNORE_INDEX
 
+    return y
+
+
+def generate(cfg: Config, threads: int = 8) -> Inputs:
+    """Draw H, W, labels and the ignore mask (in that order) for ``cfg``.  Every step is
+    integer arithmetic or correctly rounded floating point, so the bytes are the same on
+    any host."""
+    N, D, V = cfg.N, cfg.D, cfg.V
+    if cfg.h_dist == "rms":
+        H = _normal_rows(N, D, cfg.seed, _TENSOR_H, threads, _unit_rms, cfg.dtype)
+    elif cfg.h_dist == "normal":
+        H = _normal_rows(N, D, cfg.seed, _TENSOR_H, threads, lambda z: z, cfg.dtype)
+    else:
+        raise ValueError(cfg.h_dist)
+    W = _normal_rows(V, D, cfg.seed, _TENSOR_W, threads, lambda z: z * cfg.w_std, cfg.dtype)
+
+    y = _draw_labels(cfg, N, V)
+
     if cfg.dtype in ("bf16", "f16"):
         Ht, Wt = torch.from_numpy(H.view(np.int16)), torch.from_numpy(W.view(np.int16))
     elif cfg.dtype == "f32":
@@ -311,6 +319,113 @@ def generate(cfg: Config, threads: int = 8) -> Inputs:
     else:
         raise ValueError(cfg.dtype)
     return Inputs(cfg, Ht.contiguous(), Wt.contiguous(), torch.from_numpy(y).contiguous())
+
+
+# ---------------------------------------------------------------------------------
+# Materialised logits (the standalone cross-entropy over logits)
+# ---------------------------------------------------------------------------------
+
+_TENSOR_Z = 4
+_LOGIT_BLOCK_ROWS = 64  # logit rows are long (V elements): small blocks keep temporaries small
+
+
+@dataclass(frozen=True)
+class LogitConfig:
+    """Logits Z [N, V] ~ N(0, z_std^2) per element (the spread of the Llama-3-shaped head's
+    logits, 0.02 sqrt(4096) ~ 1.3, rounded up), labels and ignored rows as for Config.
+    ``ld`` > V pads each row (the pad is filled with a large value the kernels must not
+    read)."""
+
+    name: str
+    N: int
+    V: int
+    dtype: str
+    seed: int
+    z_std: float = 2.0
+    label_dist: str = "uniform"
+    zipf_s: float = 1.1
+    ignore_frac: float = 0.05
+    ignore_layout: str = "random"
+    ld: int = 0
+
+    @property
+    def n_ignored(self) -> int:
+        return int(math.floor(self.ignore_frac * self.N + 0.5))
+
+    @property
+    def pitch(self) -> int:
+        return self.ld or self.V
+
+    def describe(self) -> str:
+        return f"{self.name}: logits N={self.N}, V={self.V} (pitch {self.pitch}), {self.dtype}"
+
+
+LOGIT_CONFIGS = {
+    "ce_llama3": LogitConfig("ce_llama3", N=16384, V=128256, dtype="bf16", seed=2001),
+}
+
+
+def logit_case(N: int, V: int, dtype: str = "bf16", seed: int = 5, **kw) -> LogitConfig:
+    return LogitConfig(f"ce_N{N}_V{V}_{dtype}_s{seed}", N=N, V=V, dtype=dtype, seed=seed, **kw)
+
+
+@dataclass
+class LogitInputs:
+    """``Z`` [N, pitch] (fp32, or int16 bit patterns for bf16 / f16) and labels ``y``."""
+
+    cfg: LogitConfig
+    Z: torch.Tensor
+    y: torch.Tensor
+    _digest: str | None = field(default=None, repr=False)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[self.cfg.dtype]
+
+    def z64(self, rows=None) -> np.ndarray:
+        """Exact fp64 widening of the logits (columns < V), optionally of some rows."""
+        t = self.Z.numpy()[:, :self.cfg.V] if rows is None else self.Z.numpy()[rows, :self.cfg.V]
+        if self.cfg.dtype == "f32":
+            return t.astype(np.float64)
+        if self.cfg.dtype == "f16":
+            return t.view(np.float16).astype(np.float64)
+        return bf16_bits_to_f64(t)
+
+    def y64(self) -> np.ndarray:
+        return self.y.numpy().astype(np.int64)
+
+    def device_tensors(self, device) -> tuple[torch.Tensor, torch.Tensor]:
+        """(Z [N, V] view with row pitch ``pitch``, y) on ``device``."""
+        Z = self.Z if self.cfg.dtype == "f32" else self.Z.view(self.torch_dtype)
+        Zd = Z.to(device).contiguous()
+        return Zd[:, :self.cfg.V], self.y.to(device).contiguous()
+
+    def digest(self) -> str:
+        if self._digest is None:
+            import xxhash
+            h = xxhash.xxh3_128()
+            for t in (self.Z, self.y):
+                h.update(memoryview(t.contiguous().numpy()).cast("B"))
+            self._digest = h.hexdigest()
+        return self._digest
+
+
+def generate_logits(cfg: LogitConfig, threads: int = 8) -> LogitInputs:
+    """Draw Z, then labels and the ignore mask, for ``cfg`` (same exact-arithmetic normals
+    and rounding as ``generate``).  Pad columns hold 1e4 (finite, far above any logit)."""
+    N, V, P = cfg.N, cfg.V, cfg.pitch
+    Z = _normal_rows(N, V, cfg.seed, _TENSOR_Z, threads, lambda z: z * cfg.z_std, cfg.dtype,
+                     block_rows=_LOGIT_BLOCK_ROWS)
+    if P > V:
+        pad = np.float32(1e4)
+        fill = pad if cfg.dtype == "f32" else _ROUND16[cfg.dtype](np.array([pad], dtype=np.float32))[0]
+        Zp = np.empty((N, P), dtype=Z.dtype)
+        Zp[:, :V] = Z
+        Zp[:, V:] = fill
+        Z = Zp
+    y = _draw_labels(cfg, N, V)
+    Zt = torch.from_numpy(Z if cfg.dtype == "f32" else Z.view(np.int16)).contiguous()
+    return LogitInputs(cfg, Zt, torch.from_numpy(y).contiguous())
 
 
 def _exp_neg(x: np.ndarray) -> np.ndarray:

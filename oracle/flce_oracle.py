@@ -26,6 +26,9 @@ What it computes (all in fp64, inputs widened exactly from their fp32 / bf16 val
   first page and of the second page's pillar; g is the upstream gradient of the loss).
 * dH = dz W and dW = dz^T H: the gradient flows into the hidden states and into the
   vocabulary weight (section 3 of the first page names both).
+* ce_from_logits: the same loss, lse and logit gradient for logits given directly (the
+  row-streaming kernel of "Unsloth Kernel Architecture: Custom Triton Backpropagation and
+  QLoRA Memory Scaling", section 1, takes logits and labels).
 
 Rows are processed in blocks of ``row_block`` rows only so that a block's logits fit in
 memory; every row is computed independently from its own full logit vector.
@@ -33,7 +36,9 @@ memory; every row is computed independently from its own full logit vector.
 Pins: the test suite checks this module against closed forms (W = 0, H = 0),
 invariants (gradient rows summing to zero, shift invariance, the <dW, W> = <dH, H>
 coupling), central finite differences, PyTorch's fp64 cross_entropy + autograd on
-small shapes, and a statistical band for the loss on the paper-shaped workloads.
+small shapes, and a statistical band for the loss on the paper-shaped workloads;
+ce_from_logits against PyTorch's fp64 cross_entropy on logits and the constant-logit
+closed form.
 """
 from __future__ import annotations
 
@@ -142,3 +147,38 @@ def dW_rows(H: np.ndarray, W: np.ndarray, y: np.ndarray, vrows, lse: np.ndarray,
     P -= (y[:, None] == vrows[None, :]).astype(np.float64)
     P[y == ignore_index] = 0.0
     return (P * _scale(n_valid, g)).T @ H
+
+
+def ce_from_logits(Z: np.ndarray, y: np.ndarray, ignore_index: int = IGNORE_INDEX, g: float = 1.0,
+                   row_block: int = 256, grads: bool = True) -> dict:
+    """Cross-entropy of logits that are already materialised, Z [N, V] (fp64): per-row
+    log-sum-exp minus the label's logit, mean over valid rows, and the gradient
+    (softmax - onehot) g / N_valid ("Unsloth Kernel Architecture: Custom Triton
+    Backpropagation and QLoRA Memory Scaling", section 1 "Fused Cross-Entropy Loss with
+    Logit Streaming", whose kernel takes the logits and labels of one row at a time).
+    Rows are processed in blocks only for memory; each row uses its own full logit row.
+    Returns loss, lse, row_loss, n_valid and (grads) dZ."""
+    Z = np.asarray(Z, dtype=np.float64)
+    y = np.asarray(y, dtype=np.int64)
+    N, V = Z.shape
+    n_valid = count_valid(y, V, ignore_index)
+    s = _scale(n_valid, g)
+    lse = np.empty(N)
+    row_loss = np.zeros(N)
+    dZ = np.empty((N, V)) if grads else None
+    for r0 in range(0, N, row_block):
+        r1 = min(N, r0 + row_block)
+        Zb = Z[r0:r1]
+        yb = y[r0:r1]
+        Lb = logsumexp_rows(Zb)
+        lse[r0:r1] = Lb
+        valid = yb != ignore_index
+        idx = np.nonzero(valid)[0]
+        row_loss[r0 + idx] = Lb[idx] - Zb[idx, yb[idx]]
+        if grads:
+            dZ[r0:r1] = logit_grad(Zb, Lb, yb, s, ignore_index)
+    loss = float(row_loss.sum() / n_valid) if n_valid else 0.0
+    out = dict(loss=loss, lse=lse, row_loss=row_loss, n_valid=n_valid)
+    if grads:
+        out["dZ"] = dZ
+    return out

@@ -1,5 +1,6 @@
 """Write tests/golden/fullsize_<workload>.npz: fp64 oracle values for the full-size
-workloads (Llama-2, Mistral, Llama-3 and Qwen-2.5 shaped heads in bf16, Llama-2 in fp16).
+workloads (Llama-2, Mistral, Llama-3 and Qwen-2.5 shaped heads in bf16, Llama-2 in fp16),
+and for the cross-entropy over materialised Llama-3-shaped logits (ce_llama3).
 
 Only the oracle and the seeded input generator are used.  Stored per workload:
   digest         fingerprint of the exact input bytes (checked before comparing)
@@ -7,6 +8,8 @@ Only the oracle and the seeded input generator are used.  Stored per workload:
   lse            per-row log-sum-exp for every row
   dh_rows, dh    dH for a few rows (first, last, an ignored row, random ones)
   dw_rows, dw    dW for a few vocabulary rows (first, last, frequent labels, random)
+For ce_llama3 instead of dh/dw:
+  dz_rows, dz    dZ for a few rows (first, last, an ignored row, random ones)
 
 Usage:  python tests/golden/make_fullsize_golden.py [workload ...]
 """
@@ -22,7 +25,7 @@ sys.path.insert(0, os.path.dirname(os.path.dirname(HERE)))
 import oracle  # noqa: E402
 from linear_cross_entropy_lm_amd import inputs as I  # noqa: E402
 
-WORKLOADS = ["llama2", "mistral", "llama3", "qwen25", "llama2_f16"]
+WORKLOADS = ["llama2", "mistral", "llama3", "qwen25", "llama2_f16", "ce_llama3"]
 
 
 def pick_rows(y: np.ndarray, rng) -> np.ndarray:
@@ -44,8 +47,37 @@ def pick_vocab(y: np.ndarray, V: int, rng) -> np.ndarray:
     return np.array(sorted(vs), dtype=np.int64)
 
 
+def logits_golden(name):
+    """Loss and every row's lse in 512-row blocks (the fp64 logits of all rows would take
+    17 GB), then dZ for the sampled rows with the global N_valid."""
+    t0 = time.time()
+    cfg = I.LOGIT_CONFIGS[name]
+    inp = I.generate_logits(cfg)
+    y = inp.y64()
+    N = cfg.N
+    n_valid = oracle.count_valid(y, cfg.V, oracle.IGNORE_INDEX)
+    lse = np.empty(N)
+    row_loss = np.empty(N)
+    for r0 in range(0, N, 512):
+        r1 = min(N, r0 + 512)
+        b = oracle.ce_from_logits(inp.z64(np.arange(r0, r1)), y[r0:r1], grads=False)
+        lse[r0:r1] = b["lse"]
+        row_loss[r0:r1] = b["row_loss"]
+    loss = float(row_loss.sum() / n_valid)
+    rows = pick_rows(y, np.random.default_rng(cfg.seed))
+    dz = oracle.logit_grad(inp.z64(rows), lse[rows], y[rows], 1.0 / n_valid, oracle.IGNORE_INDEX)
+    path = os.path.join(HERE, f"fullsize_{name}.npz")
+    np.savez_compressed(path, digest=np.array(inp.digest()), loss=np.array(loss), n_valid=np.array(n_valid),
+                        lse=lse, dz_rows=rows, dz=dz)
+    print(f"{cfg.describe()}: loss {loss:.6f} n_valid {n_valid} -> {os.path.basename(path)} "
+          f"({time.time() - t0:.0f} s)", flush=True)
+
+
 def main(names):
     for name in names:
+        if name in I.LOGIT_CONFIGS:
+            logits_golden(name)
+            continue
         t0 = time.time()
         cfg = I.CONFIGS[name]
         inp = I.generate(cfg)

@@ -8,7 +8,7 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "flce.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("flce.h", "flce_ce.h")]
 
 
 @pytest.fixture(scope="module")
@@ -18,9 +18,11 @@ def B():
 
 
 def _declared():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return set(re.findall(r"\b(flce_[a-z_]+)\s*\(", text))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(flce_[a-z_]+)\s*\(", text))
+    return names
 
 
 def test_exports_every_declared_symbol(B):
@@ -139,3 +141,35 @@ def test_backward_argument_errors(B):
     assert _bwd(B, dt=0, D=6) == B.FLCE_ERR_ALIGN       # fp32 needs D % 4 == 0
     assert _bwd(B, g=A16 + 1) == B.FLCE_ERR_ALIGN
     assert _bwd(B, wsb=100) == B.FLCE_ERR_WORKSPACE
+
+
+# --- cross-entropy over materialised logits -------------------------------------------
+
+
+def test_ce_workspace_formula(B):
+    for N in (1, 255, 256, 257, 16384):
+        nblk = -(-N // 256)
+        assert B.flce_ce_workspace_bytes(N) == _r(N * 8) + _r(N * 4) + _r(nblk * 8) + 2 * _r(nblk * 4)
+    assert B.flce_ce_workspace_bytes(0) == 0
+
+
+def _ce_fwd(B, Z=A16, ld=8, y=A16, N=8, V=8, dt=1, loss=A16, lse=A16, nv=A16, st=A16, ws=A16, wsb=10**6):
+    return B.lib.flce_ce_forward(Z, ld, y, N, V, dt, -100, loss, lse, nv, st, ws, wsb, None)
+
+
+def _ce_bwd(B, Z=A16, ld=8, y=A16, lse=A16, nv=A16, g=None, N=8, V=8, dt=1, dZ=A16, ldo=8):
+    return B.lib.flce_ce_backward(Z, ld, y, lse, nv, g, N, V, dt, -100, dZ, ldo, None)
+
+
+def test_ce_argument_errors(B):
+    assert _ce_fwd(B, Z=None) == B.FLCE_ERR_INVALID_ARG
+    assert _ce_fwd(B, ld=7) == B.FLCE_ERR_INVALID_ARG          # ld < V
+    assert _ce_fwd(B, dt=5) == B.FLCE_ERR_INVALID_ARG
+    assert _ce_fwd(B, N=0) == B.FLCE_ERR_INVALID_ARG
+    assert _ce_fwd(B, Z=A16 + 2) == B.FLCE_ERR_ALIGN
+    assert _ce_fwd(B, ld=12, V=12) == B.FLCE_ERR_ALIGN         # 24-byte rows
+    assert _ce_fwd(B, wsb=16) == B.FLCE_ERR_WORKSPACE
+    assert _ce_bwd(B, dZ=None) == B.FLCE_ERR_INVALID_ARG
+    assert _ce_bwd(B, ldo=4) == B.FLCE_ERR_INVALID_ARG
+    assert _ce_bwd(B, dZ=A16 + 8) == B.FLCE_ERR_ALIGN
+    assert _ce_bwd(B, dt=0, ld=6, V=6, ldo=8) == B.FLCE_ERR_ALIGN   # 24-byte fp32 rows

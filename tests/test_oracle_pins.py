@@ -334,3 +334,63 @@ def test_pages_memory_figures_reproduce():
     assert round(fused_mb, 2) == p["fused_mb"]
     assert round((1 - fused_mb / unfused_mb) * 100, 1) == p["reduction_pct"]
     assert unfused_logit_bytes(16384, 128256, 2) == 4_202_692_608
+
+
+# --- the cross-entropy over materialised logits --------------------------------------
+
+
+def _torch_ce(Z, y, ignore_index, g):
+    Zt = torch.tensor(Z, dtype=torch.float64, requires_grad=True)
+    yt = torch.tensor(y, dtype=torch.int64)
+    loss = torch.nn.functional.cross_entropy(Zt, yt, ignore_index=ignore_index, reduction="mean")
+    (g * loss).backward()
+    lse = torch.logsumexp(Zt.detach(), dim=1).numpy()
+    return float(loss.item()), lse, Zt.grad.numpy()
+
+
+@pytest.mark.parametrize("N,V,ign,g", [(37, 113, -100, 1.0), (64, 1000, 7, -2.5), (5, 1, -100, 1.0)])
+def test_ce_from_logits_matches_torch(N, V, ign, g):
+    rng = np.random.default_rng(N * V)
+    Z = rng.normal(0.0, 3.0, size=(N, V))
+    y = rng.integers(0, V, size=N)
+    y[::4] = ign
+    if (y != ign).sum() == 0:
+        y[0] = 0 if ign != 0 else V - 1
+    ref_loss, ref_lse, ref_dZ = _torch_ce(Z, y, ign, g)
+    got = oracle.ce_from_logits(Z, y, ignore_index=ign, g=g, row_block=16)
+    assert abs(got["loss"] - ref_loss) <= 1e-12 * max(1.0, abs(ref_loss))
+    assert np.allclose(got["lse"], ref_lse, rtol=0, atol=1e-12)
+    assert np.allclose(got["dZ"], ref_dZ, rtol=0, atol=1e-15)
+
+
+def test_ce_from_logits_constant_rows():
+    """Equal logits in a row: lse = c + ln V, loss = ln V, dZ = (1/V - onehot) g / N_valid."""
+    N, V, g = 9, 50, 3.0
+    Z = np.repeat(np.arange(N, dtype=np.float64)[:, None] * 0.75 - 2.0, V, axis=1)
+    y = np.arange(N) % V
+    y[4] = -100
+    got = oracle.ce_from_logits(Z, y, g=g)
+    nv = N - 1
+    assert np.allclose(got["lse"], Z[:, 0] + math.log(V), rtol=0, atol=1e-13)
+    assert abs(got["loss"] - math.log(V)) <= 1e-13
+    expect = np.full((N, V), 1.0 / V)
+    valid = np.nonzero(y != -100)[0]
+    expect[valid, y[valid]] -= 1.0
+    expect[4] = 0.0
+    assert np.allclose(got["dZ"], expect * g / nv, rtol=0, atol=1e-15)
+
+
+def test_ce_from_logits_agrees_with_fused_definition():
+    """On Z = H W^T the two oracle entry points give the same loss and lse, and the
+    chain rule dH = dZ W, dW = dZ^T H."""
+    rng = np.random.default_rng(3)
+    H = rng.normal(size=(20, 12))
+    W = rng.normal(0, 0.3, size=(31, 12))
+    y = rng.integers(0, 31, size=20)
+    y[3] = -100
+    fused = oracle.forward_backward(H, W, y, g=1.5)
+    ce = oracle.ce_from_logits(H @ W.T, y, g=1.5)
+    assert abs(fused["loss"] - ce["loss"]) <= 1e-13
+    assert np.allclose(fused["lse"], ce["lse"], atol=1e-13)
+    assert np.allclose(fused["dH"], ce["dZ"] @ W, atol=1e-14)
+    assert np.allclose(fused["dW"], ce["dZ"].T @ H, atol=1e-14)
