@@ -56,7 +56,8 @@ extern "C" {
 typedef enum flce_status {
   FLCE_OK = 0,
   FLCE_ERR_INVALID_ARG = 1, /* null pointer, size < 1 or too large, unknown dtype */
-  FLCE_ERR_ALIGN = 2,       /* misaligned pointer, or D not a multiple of 8 (bf16, fp16) / 4 (fp32) */
+  FLCE_ERR_ALIGN = 2,       /* misaligned pointer, or D (flce_*) or a row pitch (flce_ce_*) not a
+                               multiple of 8 elements (bf16, fp16) / 4 (fp32) */
   FLCE_ERR_WORKSPACE = 3,   /* workspace smaller than the call needs */
   FLCE_ERR_HIP = 4          /* a kernel launch failed (hipGetLastError after launching) */
 } flce_status;

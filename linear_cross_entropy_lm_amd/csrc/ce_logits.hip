@@ -6,13 +6,23 @@
 // streams the vocabulary in blocks, keeping a running maximum and a running sum of
 // exponentials; the row loss is the log-sum-exp minus the label's logit.
 //
-// Layout of the work: one 256-thread workgroup per row.  Thread t takes the 16-byte chunks
-// t, t + 256, t + 512, ... of the row, so each wave-wide load is 1 KB of consecutive
-// bytes, four chunks in flight per thread.  Each thread keeps its own (max, sum of
-// exp(z - max)): a chunk that raises the maximum rescales the sum once, then adds its
-// elements' exponentials.  The 256 states merge in a fixed order (wave butterfly, then
-// the four waves through LDS), so results are deterministic.  Every logit is read once in
-// the forward and read and written once in the backward: both kernels are HBM-bound.
+// Every logit is read once in the forward and read and written once in the backward: both
+// kernels are HBM-bound, and both stream with non-temporal loads and stores (each byte is
+// touched once; keeping it would only evict other data).
+//
+// Forward: one 512-thread workgroup per row (rows taken in a grid-stride loop).  Thread t
+// takes the 16-byte chunks t, t + 512, ... of the row, so each wave-wide load is 1 KB of
+// consecutive bytes, and keeps its own (max, sum of exp(z - max)).  Chunks that lie wholly
+// inside the row take an unmasked path; only the last chunk of a row is masked.  The 512
+// states merge in a fixed order (wave butterfly, then the eight waves through LDS), so
+// results are deterministic.
+//
+// Backward: each row is cut into pieces of 512 chunks (8 KB of 16-bit logits), one piece
+// per workgroup, one chunk per thread; consecutive workgroups take consecutive pieces, so
+// the workgroups in flight read and write one contiguous window of memory rather than
+// thousands of separate row streams (measured: 6.1 TB/s against 5.0 TB/s for one
+// workgroup per row).  It needs only the row's lse and label, so pieces are independent.
+//
 // Loads go through buffer descriptors over the row's V elements rounded up to whole dwords
 // (the range check drops any dword that crosses the end, so an exact 16-bit range would
 // lose element V - 1 of an odd row; the rounding stays inside the row pitch, which is a
@@ -37,11 +47,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kThreads = 256;
-constexpr int kInFlight = 4;  // chunks loaded ahead per thread
+constexpr int kThreads = 512;           // both kernels
+constexpr int kMaxGrid = 1 << 20;       // workgroups per launch (work-items stay below 2^32)
+constexpr int kLoadAux = 2;             // buffer cache policy: non-temporal
+constexpr int kStoreAux = 2;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr u32 kOOB = 0x7ffffff0u;
 
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
@@ -133,72 +144,79 @@ template <> struct Fmt<FLCE_F16> {
   }
 };
 
-// Forward, one workgroup per row: lse[n], and the row's loss term and flag (1 valid,
-// 2 label out of range, 0 ignored) for the fixed-order mean.
+// Forward: lse[n], and the row's loss term and flag (1 valid, 2 label out of range,
+// 0 ignored) for the fixed-order mean.  Workgroup b takes rows b, b + grid, ...
 template <int DT>
 __global__ __launch_bounds__(kThreads) void ce_rows_fwd(const char* __restrict__ Z, int64_t ld_bytes,
-                                                        const int64_t* __restrict__ y, int V, int64_t ignore_index,
-                                                        float* __restrict__ lse, double* __restrict__ rloss,
-                                                        int* __restrict__ rflag) {
+                                                        const int64_t* __restrict__ y, int N, int V,
+                                                        int64_t ignore_index, float* __restrict__ lse,
+                                                        double* __restrict__ rloss, int* __restrict__ rflag) {
   using F = Fmt<DT>;
   constexpr int K = F::K;
-  const int n = blockIdx.x;
-  const char* row = Z + (int64_t)n * ld_bytes;
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(row, load_bytes(V, F::ES));
-  const int nchunks = (V + K - 1) / K;
-  float m = -__builtin_inff(), s = 0.f;
-  for (int c0 = threadIdx.x; c0 < nchunks; c0 += kInFlight * kThreads) {
-    u32x4 w[kInFlight];
-#pragma unroll
-    for (int j = 0; j < kInFlight; ++j) {
-      const int c = c0 + j * kThreads;
-      w[j] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(c < nchunks ? (u32)c * 16u : kOOB), 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < kInFlight; ++j) {
-      const int i0 = (c0 + j * kThreads) * K;  // >= V for a chunk past the row: all masked
+  __shared__ float2 red[kThreads / 64];
+  const int nchunks = (V + K - 1) / K, nfull = V / K;
+  for (int n = blockIdx.x; n < N; n += gridDim.x) {
+    const char* row = Z + (int64_t)n * ld_bytes;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(row, load_bytes(V, F::ES));
+    float m = -__builtin_inff(), s = 0.f;
+    int c = threadIdx.x;
+    // Chunks wholly inside the row.  The new maximum is taken first; a maximum still at
+    // -inf (every logit so far -inf) uses 0 as the reference so no inf - inf appears.
+    for (; c < nfull; c += kThreads) {
       float z[K];
-      F::decode(w[j], z);
-      const bool full = i0 + K <= V;
-      float cm = -__builtin_inff();
+      F::decode(__builtin_amdgcn_raw_buffer_load_b128(r, (int)((u32)c * 16u), 0, kLoadAux), z);
+      float cm = m;
+#pragma unroll
+      for (int e = 0; e < K; ++e) cm = fmaxf(cm, z[e]);
+      const float mb = (cm == -__builtin_inff() ? 0.f : cm) * kLog2e;
+      float acc = s * hw_exp2(__builtin_fmaf(m, kLog2e, -mb));
+#pragma unroll
+      for (int e = 0; e < K; ++e) acc += hw_exp2(__builtin_fmaf(z[e], kLog2e, -mb));
+      s = acc;
+      m = cm;
+    }
+    // The chunk holding the row's ragged end, element masks.
+    if (c < nchunks) {
+      const int i0 = c * K;
+      float z[K];
+      F::decode(__builtin_amdgcn_raw_buffer_load_b128(r, (int)((u32)c * 16u), 0, kLoadAux), z);
+      float cm = m;
 #pragma unroll
       for (int e = 0; e < K; ++e)
-        if (full || i0 + e < V) cm = fmaxf(cm, z[e]);
-      const float mn = fmaxf(m, cm);
-      if (mn != -__builtin_inff()) {
-        s *= hw_exp2((m - mn) * kLog2e);  // m = -inf: s is 0 and stays 0
-        const float mb = mn * kLog2e;
+        if (i0 + e < V) cm = fmaxf(cm, z[e]);
+      const float mb = (cm == -__builtin_inff() ? 0.f : cm) * kLog2e;
+      float acc = s * hw_exp2(__builtin_fmaf(m, kLog2e, -mb));
 #pragma unroll
-        for (int e = 0; e < K; ++e)
-          if (full || i0 + e < V) s += hw_exp2(__builtin_fmaf(z[e], kLog2e, -mb));
-        m = mn;
-      }
+      for (int e = 0; e < K; ++e)
+        if (i0 + e < V) acc += hw_exp2(__builtin_fmaf(z[e], kLog2e, -mb));
+      s = acc;
+      m = cm;
     }
-  }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) lse_merge(m, s, __shfl_xor(m, off), __shfl_xor(s, off));
-  __shared__ float2 red[kThreads / 64];
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = make_float2(m, s);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float M = red[0].x, S = red[0].y;
+    for (int off = 32; off >= 1; off >>= 1) lse_merge(m, s, __shfl_xor(m, off), __shfl_xor(s, off));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = make_float2(m, s);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float M = red[0].x, S = red[0].y;
 #pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) lse_merge(M, S, red[w].x, red[w].y);
-    const float L = M + hw_log2(S) * kLn2;
-    lse[n] = L;
-    const int64_t lab = y[n];
-    double l = 0.0;
-    int flag = 0;
-    if (lab != ignore_index) {
-      if (lab >= 0 && lab < V) {
-        l = (double)L - (double)F::one(row + lab * F::ES);
-        flag = 1;
-      } else {
-        flag = 2;
+      for (int w = 1; w < kThreads / 64; ++w) lse_merge(M, S, red[w].x, red[w].y);
+      const float L = M + hw_log2(S) * kLn2;
+      lse[n] = L;
+      const int64_t lab = y[n];
+      double l = 0.0;
+      int flag = 0;
+      if (lab != ignore_index) {
+        if (lab >= 0 && lab < V) {
+          l = (double)L - (double)F::one(row + lab * F::ES);
+          flag = 1;
+        } else {
+          flag = 2;
+        }
       }
+      rloss[n] = l;
+      rflag[n] = flag;
     }
-    rloss[n] = l;
-    rflag[n] = flag;
+    __syncthreads();  // red is reused by the next row
   }
 }
 
@@ -262,61 +280,54 @@ __global__ __launch_bounds__(256) void ce_finalize(const double* __restrict__ bl
   }
 }
 
-// Backward, one workgroup per row: dZ = (exp(z - lse) - onehot) * c, c = g / N_valid for
-// valid rows and 0 otherwise.  As 2^(z log2(e) - e2) with e2 = lse log2(e) - log2|c| and
-// the sign of c applied by xor; e2 = +inf writes exact zeros.  Each thread reads a chunk
-// before writing it, so dZ may alias Z.  The chunk holding v = V - 1 is written element by
-// element so columns past V are left alone.
+// Backward: dZ = (exp(z - lse) - onehot) * c, c = g / N_valid for valid rows and 0
+// otherwise.  As 2^(z log2(e) - e2) with e2 = lse log2(e) - log2|c| and the sign of c
+// applied by xor; e2 = +inf writes exact zeros.  Workgroup b takes pieces b, b + grid, ...;
+// piece q is chunk range [512 (q mod P), 512 (q mod P) + 512) of row q / P (P pieces per
+// row), one chunk per thread.  Each thread reads its chunk before writing it, so dZ may
+// alias Z.  The chunk holding v = V - 1 is written element by element so columns past V
+// are left alone.
 template <int DT>
 __global__ __launch_bounds__(kThreads) void ce_rows_bwd(const char* Z, int64_t ld_bytes, const int64_t* __restrict__ y,
                                                         const float* __restrict__ lse,
                                                         const int32_t* __restrict__ n_valid,
-                                                        const float* __restrict__ grad, int V, int64_t ignore_index,
-                                                        char* dZ, int64_t ldo_bytes) {
+                                                        const float* __restrict__ grad, int V, int P, int64_t pieces,
+                                                        int64_t ignore_index, char* dZ, int64_t ldo_bytes) {
   using F = Fmt<DT>;
   constexpr int K = F::K;
-  const int n = blockIdx.x;
   const int nv = *n_valid;
   const float g = grad ? *grad : 1.f;
   const float sv = nv > 0 ? g / (float)nv : 0.f;
-  const int64_t lab = y[n];
-  const bool ok = lab != ignore_index && lab >= 0 && lab < V;
-  const float c = ok ? sv : 0.f;
-  const float e2 = c != 0.f ? lse[n] * kLog2e - hw_log2(fabsf(c)) : __builtin_inff();
-  const u32 sgn = __builtin_bit_cast(u32, c) & 0x80000000u;
-  const int lab_i = ok ? (int)lab : -1;
-  const __amdgpu_buffer_rsrc_t ri = make_rsrc(Z + (int64_t)n * ld_bytes, load_bytes(V, F::ES));
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc(dZ + (int64_t)n * ldo_bytes, (u32)V * (u32)F::ES);
   const int nchunks = (V + K - 1) / K;
-  for (int c0 = threadIdx.x; c0 < nchunks; c0 += kInFlight * kThreads) {
-    u32x4 w[kInFlight];
+  for (int64_t q = blockIdx.x; q < pieces; q += gridDim.x) {
+    const int n = (int)(q / P);
+    const int ch = (int)(q - (int64_t)n * P) * kThreads + (int)threadIdx.x;
+    const int64_t lab = y[n];
+    const bool ok = lab != ignore_index && lab >= 0 && lab < V;
+    const float c = ok ? sv : 0.f;
+    const float e2 = c != 0.f ? lse[n] * kLog2e - hw_log2(fabsf(c)) : __builtin_inff();
+    const u32 sgn = __builtin_bit_cast(u32, c) & 0x80000000u;
+    const int lab_i = ok ? (int)lab : -1;
+    if (ch >= nchunks) continue;
+    const __amdgpu_buffer_rsrc_t ri = make_rsrc(Z + (int64_t)n * ld_bytes, load_bytes(V, F::ES));
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(dZ + (int64_t)n * ldo_bytes, (u32)V * (u32)F::ES);
+    float z[K], d[K];
+    F::decode(__builtin_amdgcn_raw_buffer_load_b128(ri, (int)((u32)ch * 16u), 0, kLoadAux), z);
+    const int i0 = ch * K;
 #pragma unroll
-    for (int j = 0; j < kInFlight; ++j) {
-      const int ch = c0 + j * kThreads;
-      w[j] = __builtin_amdgcn_raw_buffer_load_b128(ri, (int)(ch < nchunks ? (u32)ch * 16u : kOOB), 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < kInFlight; ++j) {
-      const int ch = c0 + j * kThreads;
-      if (ch >= nchunks) break;
-      const int i0 = ch * K;
-      float z[K], d[K];
-      F::decode(w[j], z);
+    for (int e = 0; e < K; ++e)
+      d[e] = __builtin_bit_cast(float, __builtin_bit_cast(u32, hw_exp2(__builtin_fmaf(z[e], kLog2e, -e2))) ^ sgn);
+    if (lab_i >= i0 && lab_i < i0 + K) {
 #pragma unroll
       for (int e = 0; e < K; ++e)
-        d[e] = __builtin_bit_cast(float, __builtin_bit_cast(u32, hw_exp2(__builtin_fmaf(z[e], kLog2e, -e2))) ^ sgn);
-      if (lab_i >= i0 && lab_i < i0 + K) {
+        if (i0 + e == lab_i) d[e] -= c;
+    }
+    if (i0 + K <= V) {
+      __builtin_amdgcn_raw_buffer_store_b128(F::encode(d), ro, (int)((u32)ch * 16u), 0, kStoreAux);
+    } else {
 #pragma unroll
-        for (int e = 0; e < K; ++e)
-          if (i0 + e == lab_i) d[e] -= c;
-      }
-      if (i0 + K <= V) {
-        __builtin_amdgcn_raw_buffer_store_b128(F::encode(d), ro, (int)((u32)ch * 16u), 0, 0);
-      } else {
-#pragma unroll
-        for (int e = 0; e < K; ++e)
-          if (i0 + e < V) F::store_one(ro, (u32)(i0 + e) * (u32)F::ES, d[e]);
-      }
+      for (int e = 0; e < K; ++e)
+        if (i0 + e < V) F::store_one(ro, (u32)(i0 + e) * (u32)F::ES, d[e]);
     }
   }
 }
@@ -365,8 +376,9 @@ flce_status ce_forward_impl(const char* Z, int64_t ld, const int64_t* y, int N, 
   int* bc = reinterpret_cast<int*>(ws + L.bc);
   int* bb = reinterpret_cast<int*>(ws + L.bb);
   (void)hipGetLastError();
-  ce_rows_fwd<DT><<<dim3((unsigned)N), dim3(kThreads), 0, s>>>(Z, ld * Fmt<DT>::ES, y, V, ignore_index, lse, rloss,
-                                                               rflag);
+  const int grid = N < kMaxGrid ? N : kMaxGrid;
+  ce_rows_fwd<DT><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(Z, ld * Fmt<DT>::ES, y, N, V, ignore_index, lse,
+                                                                  rloss, rflag);
   ce_block_sum<<<dim3((unsigned)L.nblk), dim3(256), 0, s>>>(rloss, rflag, N, bl, bc, bb);
   ce_finalize<<<dim3(1), dim3(256), 0, s>>>(bl, bc, bb, L.nblk, loss, n_valid, dev_status);
   return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
@@ -377,8 +389,11 @@ flce_status ce_backward_impl(const char* Z, int64_t ld, const int64_t* y, const 
                              const float* grad, int N, int V, int64_t ignore_index, char* dZ, int64_t ld_out,
                              hipStream_t s) {
   (void)hipGetLastError();
-  ce_rows_bwd<DT><<<dim3((unsigned)N), dim3(kThreads), 0, s>>>(Z, ld * Fmt<DT>::ES, y, lse, n_valid, grad, V,
-                                                               ignore_index, dZ, ld_out * Fmt<DT>::ES);
+  const int P = ((V + Fmt<DT>::K - 1) / Fmt<DT>::K + kThreads - 1) / kThreads;
+  const int64_t pieces = (int64_t)N * P;
+  const int grid = pieces < kMaxGrid ? (int)pieces : kMaxGrid;
+  ce_rows_bwd<DT><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(Z, ld * Fmt<DT>::ES, y, lse, n_valid, grad, V, P,
+                                                                  pieces, ignore_index, dZ, ld_out * Fmt<DT>::ES);
   return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 

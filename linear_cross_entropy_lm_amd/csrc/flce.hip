@@ -1279,7 +1279,7 @@ const char* flce_status_string(int status) {
   switch (status) {
     case FLCE_OK: return "FLCE_OK";
     case FLCE_ERR_INVALID_ARG: return "FLCE_ERR_INVALID_ARG: null pointer, invalid size or unknown dtype";
-    case FLCE_ERR_ALIGN: return "FLCE_ERR_ALIGN: misaligned pointer or D not a multiple of 8 (bf16) / 4 (fp32)";
+    case FLCE_ERR_ALIGN: return "FLCE_ERR_ALIGN: misaligned pointer, or D / row pitch not a multiple of 16 bytes of elements";
     case FLCE_ERR_WORKSPACE: return "FLCE_ERR_WORKSPACE: workspace too small";
     case FLCE_ERR_HIP: return "FLCE_ERR_HIP: kernel launch failed";
     default: return "unknown flce status";

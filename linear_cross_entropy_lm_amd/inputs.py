@@ -329,6 +329,11 @@ _TENSOR_Z = 4
 _LOGIT_BLOCK_ROWS = 64  # logit rows are long (V elements): small blocks keep temporaries small
 
 
+def _logit_block_rows(V: int) -> int:
+    """Rows per generator stream: 64 for long rows, more for short ones (>= 2^16 values)."""
+    return max(_LOGIT_BLOCK_ROWS, (1 << 16) // max(V, 1))
+
+
 @dataclass(frozen=True)
 class LogitConfig:
     """Logits Z [N, V] ~ N(0, z_std^2) per element (the spread of the Llama-3-shaped head's
@@ -415,7 +420,7 @@ def generate_logits(cfg: LogitConfig, threads: int = 8) -> LogitInputs:
     and rounding as ``generate``).  Pad columns hold 1e4 (finite, far above any logit)."""
     N, V, P = cfg.N, cfg.V, cfg.pitch
     Z = _normal_rows(N, V, cfg.seed, _TENSOR_Z, threads, lambda z: z * cfg.z_std, cfg.dtype,
-                     block_rows=_LOGIT_BLOCK_ROWS)
+                     block_rows=_logit_block_rows(V))
     if P > V:
         pad = np.float32(1e4)
         fill = pad if cfg.dtype == "f32" else _ROUND16[cfg.dtype](np.array([pad], dtype=np.float32))[0]

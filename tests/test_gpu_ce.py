@@ -2,8 +2,8 @@
 fp64 oracle (oracle.ce_from_logits), element by element, on seeded logits with ragged
 row lengths, padded rows and the edge cases; plus the Llama-3-shaped full size.
 
-Tolerances (relative): loss and lse 1e-5 for every dtype (each row's exponentials sum in
-fp32; inputs are identical on both sides); dZ Frobenius 1e-5 for fp32 output, 4e-3 for
+Tolerances: loss relative 1e-5 and lse within 1e-5 * max(|lse|, 1) for every dtype (each
+row's exponentials sum in fp32; inputs are identical on both sides); dZ Frobenius 1e-5 for fp32 output, 4e-3 for
 bf16 (rounding, 2^-9) and 1e-3 for fp16 (2^-11).  fp16 cases run with a loss scale
 g = 4096: at g = 1, dZ ~ p / N_valid falls below fp16's smallest normal.
 """
@@ -73,8 +73,11 @@ def check(got, inp, g, ignore_index=-100):
         assert abs(got["loss"] - ref["loss"]) <= 1e-5 * abs(ref["loss"])
     else:
         assert got["loss"] == 0.0
-    lse_err = float(np.max(np.abs(got["lse"] - ref["lse"]) / np.maximum(np.abs(ref["lse"]), 1e-30)))
-    assert lse_err <= 1e-5, lse_err
+    # fp32 rounding of a log-sum-exp scales with its terms, not with lse itself, which can
+    # sit near 0 for short rows: error relative to max(|lse|, 1)
+    lse_abs = np.abs(got["lse"] - ref["lse"])
+    lse_err = float(np.max(lse_abs / np.maximum(np.abs(ref["lse"]), 1.0)))
+    assert lse_err <= 1e-5, (lse_err, float(lse_abs.max()))
     err = rel_fro(got["dZ"], ref["dZ"]) if np.linalg.norm(ref["dZ"]) > 0 else float(np.abs(got["dZ"]).max())
     assert err <= TOL_GRAD[inp.cfg.dtype], err
     _say("errors", dict(lse=lse_err, dZ=err))
@@ -142,6 +145,18 @@ def test_ce_all_ignored_and_bad_labels():
     y_ref = y.numpy().copy()
     y_ref[10], y_ref[20] = -100, -100
     check(got, I.LogitInputs(cfg, inp.Z, torch.from_numpy(y_ref)), 1.0)
+
+
+def test_ce_rows_beyond_one_launch_grid():
+    """1.1M rows: more rows and backward pieces than one launch's 2^20 workgroups, so both
+    kernels loop over their work."""
+    cfg = I.logit_case(1_100_000, 5, "bf16", seed=45, ld=8)
+    _say("case", cfg.describe())
+    inp = I.generate_logits(cfg)
+    got = run_ce(inp, out_pad=True)
+    check(got, inp, 1.0)
+    assert got["status"] == 0
+    assert np.isnan(got["pad"]).all(), "columns past V were written"
 
 
 def test_ce_bitwise_deterministic():
