@@ -394,3 +394,90 @@ def test_ce_from_logits_agrees_with_fused_definition():
     assert np.allclose(fused["lse"], ce["lse"], atol=1e-13)
     assert np.allclose(fused["dH"], ce["dZ"] @ W, atol=1e-14)
     assert np.allclose(fused["dW"], ce["dZ"].T @ H, atol=1e-14)
+
+
+# --- RMSNorm (oracle/norm_oracle.py) ------------------------------------------------
+
+
+def _norm_case(N, D, seed, uniform_gamma=False):
+    rng = np.random.default_rng(seed)
+    X = rng.normal(0.0, 1.5, size=(N, D))
+    gamma = np.full(D, 0.8) if uniform_gamma else rng.normal(1.0, 0.3, size=D)
+    dH = rng.normal(0.0, 1.0, size=(N, D))
+    return X, gamma, dH
+
+
+@pytest.mark.parametrize("N,D,eps", [(7, 16, 0.0), (33, 257, 1e-6), (4, 1, 1e-5)])
+def test_rmsnorm_matches_torch_rms_norm(N, D, eps):
+    """PyTorch's fp64 rms_norm (weight = gamma) and its autograd."""
+    X, gamma, dH = _norm_case(N, D, N * D)
+    Xt = torch.tensor(X, requires_grad=True)
+    gt = torch.tensor(gamma, requires_grad=True)
+    Ht = torch.nn.functional.rms_norm(Xt, (D,), weight=gt, eps=eps)
+    Ht.backward(torch.tensor(dH))
+    f = oracle.rmsnorm_forward(X, gamma, eps)
+    b = oracle.rmsnorm_backward(X, gamma, dH, eps)
+    assert np.allclose(f["H"], Ht.detach().numpy(), rtol=1e-13, atol=1e-14)
+    assert np.allclose(b["dX"], Xt.grad.numpy(), rtol=1e-12, atol=1e-13)
+    assert np.allclose(b["dgamma"], gt.grad.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_rmsnorm_backward_matches_page_formula_at_uniform_gamma():
+    """With the same gamma on every channel the page's printed gradient is exact:
+    dx = gamma / RMS * (dy - x * sum(x dy) / (d RMS^2))."""
+    X, gamma, dH = _norm_case(9, 40, 11, uniform_gamma=True)
+    eps = 1e-5
+    d = X.shape[1]
+    rms = np.sqrt(np.mean(X * X, axis=1) + eps)[:, None]
+    page = gamma[None, :] / rms * (dH - X * np.sum(X * dH, axis=1, keepdims=True) / (d * rms ** 2))
+    assert np.allclose(oracle.rmsnorm_backward(X, gamma, dH, eps)["dX"], page, rtol=1e-13, atol=1e-14)
+
+
+def test_rmsnorm_scale_invariance():
+    """eps = 0: H(a X) = H(X) for a > 0, so <dX_n, x_n> = 0 on every row; eps > 0:
+    <dX_n, x_n> = eps * s_n / r_n^3 with s_n = sum_i gamma_i x_i dy_i."""
+    X, gamma, dH = _norm_case(12, 64, 5)
+    f1 = oracle.rmsnorm_forward(X, gamma, 0.0)["H"]
+    f2 = oracle.rmsnorm_forward(3.7 * X, gamma, 0.0)["H"]
+    assert np.allclose(f1, f2, rtol=1e-14, atol=1e-14)
+    dX = oracle.rmsnorm_backward(X, gamma, dH, 0.0)["dX"]
+    scale = np.linalg.norm(dX, axis=1) * np.linalg.norm(X, axis=1)
+    assert np.all(np.abs(np.sum(dX * X, axis=1)) <= 1e-13 * scale)
+    eps = 0.3
+    dX = oracle.rmsnorm_backward(X, gamma, dH, eps)["dX"]
+    r = np.sqrt(np.mean(X * X, axis=1) + eps)
+    s = np.sum(gamma[None, :] * X * dH, axis=1)
+    assert np.allclose(np.sum(dX * X, axis=1), eps * s / r ** 3, rtol=1e-12, atol=1e-13)
+
+
+def test_rmsnorm_gamma_coupling():
+    """sum_j gamma_j dgamma_j = sum_n <dy_n, y_n> (both equal sum dy * x * gamma / r)."""
+    X, gamma, dH = _norm_case(20, 48, 6)
+    H = oracle.rmsnorm_forward(X, gamma, 1e-6)["H"]
+    dg = oracle.rmsnorm_backward(X, gamma, dH, 1e-6)["dgamma"]
+    assert abs(np.dot(gamma, dg) - np.sum(dH * H)) <= 1e-12 * np.sum(np.abs(dH * H))
+
+
+def test_rmsnorm_finite_differences():
+    """Central differences of L = <dY, H(X, gamma)> in every entry of X and gamma."""
+    X, gamma, dH = _norm_case(3, 6, 8)
+    eps, h = 1e-4, 1e-6
+
+    def L(Xv, gv):
+        return float(np.sum(dH * oracle.rmsnorm_forward(Xv, gv, eps)["H"]))
+
+    b = oracle.rmsnorm_backward(X, gamma, dH, eps)
+    num_dX = np.zeros_like(X)
+    for idx in np.ndindex(X.shape):
+        Xp, Xm = X.copy(), X.copy()
+        Xp[idx] += h
+        Xm[idx] -= h
+        num_dX[idx] = (L(Xp, gamma) - L(Xm, gamma)) / (2 * h)
+    num_dg = np.zeros_like(gamma)
+    for j in range(len(gamma)):
+        gp, gm = gamma.copy(), gamma.copy()
+        gp[j] += h
+        gm[j] -= h
+        num_dg[j] = (L(X, gp) - L(X, gm)) / (2 * h)
+    assert np.linalg.norm(num_dX - b["dX"]) <= 1e-7 * np.linalg.norm(b["dX"])
+    assert np.linalg.norm(num_dg - b["dgamma"]) <= 1e-7 * np.linalg.norm(b["dgamma"])
