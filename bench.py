@@ -6,6 +6,10 @@
 One step = flce_forward + flce_backward over one batch of synthetic input already
 resident in HBM (loss, lse, dH, dW all produced).  Prints one JSON line.
 
+--path norm measures the RMSNorm that produces H (include/flce_norm.h): one step =
+flce_rmsnorm_forward + flce_rmsnorm_backward at 16384 x 4096 bf16; its roofline is the
+backward call (rms_bwd and its two small dgamma passes) against the HBM peak.
+
 --path ce measures the cross-entropy over materialised logits instead (include/flce_ce.h):
 one step = flce_ce_forward + flce_ce_backward over bf16 logits [16384, 128256] in HBM
 (loss, lse, dZ into a separate buffer); its roofline is the backward kernel (ce_rows_bwd)
@@ -34,6 +38,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fused linear-CE fwd+bwd tokens/s at N=16384,D=4096,V=128256; % bf16 MFMA peak"
 METRIC_CE = "cross-entropy over materialised logits fwd+bwd tokens/s at N=16384,V=128256; % HBM peak"
+METRIC_NORM = "RMSNorm fwd+fused bwd tokens/s at N=16384,D=4096; % HBM peak"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "linear_cross_entropy_lm_amd", "csrc")
@@ -43,6 +48,8 @@ PATHS = {
               os.path.join(CSRC, "flce.hip")),
     "ce": ("ce_rows_bwd", "ce_llama3", os.path.join(ROOT, "profiles", "ce_rows_bwd_ce_llama3_traffic.json"),
            os.path.join(CSRC, "ce_logits.hip")),
+    "norm": ("rms_bwd", "norm_llama3", os.path.join(ROOT, "profiles", "rms_bwd_norm_llama3_traffic.json"),
+             os.path.join(CSRC, "rmsnorm.hip")),
 }
 
 
@@ -69,6 +76,17 @@ def ce_row_bytes(V: int, es: int) -> tuple[int, int]:
     row (V es) and its label (8) and writes lse (4), the row's loss term (8) and flag (4);
     backward reads the row, label and lse and writes the row of dZ (V es)."""
     return V * es + 24, 2 * V * es + 12
+
+
+def norm_bytes(N: int, D: int, es: int, grid: int) -> tuple[int, int]:
+    """Algorithmic HBM bytes of the RMSNorm calls: forward reads X and gamma and writes H and
+    rstd; the backward call reads X, dH, rstd and gamma, writes dX, and writes then reads
+    the fp32 dgamma partials (one row of D per backward workgroup, then one per 32 of those)
+    and writes dgamma."""
+    groups = -(-grid // 32)
+    fwd = 2 * N * D * es + 4 * N + D * es
+    bwd = 3 * N * D * es + 4 * N + D * es + 2 * grid * D * 4 + 2 * groups * D * 4 + D * 4
+    return fwd, bwd
 
 
 def _counter_per_dispatch(csv_dir: str, counter: str, kernel_prefix: str):
@@ -279,6 +297,79 @@ def run_ce(args) -> dict:
     return out
 
 
+def cpu_baseline_norm(inp) -> dict:
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    X, g, dH = inp.x64(), inp.gamma64(), inp.dh64()
+    t0 = time.perf_counter()
+    oracle.rmsnorm_forward(X, g, inp.cfg.eps)
+    oracle.rmsnorm_backward(X, g, dH, inp.cfg.eps)
+    dt = time.perf_counter() - t0
+    return {"value": inp.cfg.N / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"all {inp.cfg.N} rows, D={inp.cfg.D}: fp64 H, rstd, dX and dgamma in {dt:.1f} s",
+            "seconds": dt}
+
+
+def run_norm(args) -> dict:
+    import torch
+    from linear_cross_entropy_lm_amd import binding as B
+    from linear_cross_entropy_lm_amd import inputs as I
+
+    cfg = I.NORM_CONFIGS[args.workload or "norm_llama3"]
+    inp = I.generate_norm(cfg)
+    dev = "cuda:0"
+    X, g, dH = inp.device_tensors(dev)
+    N, D = cfg.N, cfg.D
+    es = X.element_size()
+    H = torch.empty_like(X)
+    rstd = torch.empty(N, dtype=torch.float32, device=dev)
+    dX = torch.empty_like(X)
+    dg = torch.empty(D, dtype=torch.float32, device=dev)
+    ws = torch.empty(B.flce_rmsnorm_workspace_bytes(N, D), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        B.flce_rmsnorm_forward(X, g, H, rstd, cfg.eps, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        B.flce_rmsnorm_backward(X, g, rstd, dH, dX, dg, ws, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    ms, fwd_ms, step_ms, peak_delta = _time_steps(args, step, stream)
+    bwd_ms = ms - fwd_ms
+    fwd_b, bwd_b = norm_bytes(N, D, es, min(N, 512))
+    achieved = bwd_b / (bwd_ms * 1e-3) / 1e9
+    out = _common(args, METRIC_NORM, N / (ms * 1e-3), ms, cfg.dtype,
+                  f"synthetic: seeded X ~ N(0, {cfg.x_std}^2), gamma ~ 1 + N(0, {cfg.gamma_std}^2), "
+                  f"dH ~ N(0, {cfg.dh_std}^2), eps {cfg.eps:g}",
+                  {"workload": f"{cfg.name}: RMSNorm of the hidden states before the lm_head, fwd + fused bwd",
+                   "N": N, "D": D, "parallelism": "single GPU"})
+    out.update({
+        "hbm_peak_frac": (fwd_b + bwd_b) / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "fwd_ms": fwd_ms,
+        "bwd_ms": bwd_ms,
+        "fwd_gbs": fwd_b / (fwd_ms * 1e-3) / 1e9,
+        "step_ms_median": step_ms[len(step_ms) // 2],
+        "step_ms_min": step_ms[0],
+        "step_ms_max": step_ms[-1],
+        "torch_peak_alloc_delta_bytes": int(peak_delta),
+        "roofline": {"kernel": "rms_bwd (+ 2 dgamma passes)", "bound": "hbm", "achieved": achieved,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": load_traffic("norm")},
+        "cpu_baseline": None,
+    })
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_norm(inp)
+    return out
+
+
 def _time_steps(args, step, stream):
     """W warmup steps, one step under torch's allocator peak tracking (the library
     allocates nothing, so the peak stays at what is already held), then K timed steps
@@ -315,8 +406,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--path", choices=sorted(PATHS), default="fused",
                     help="fused: lm_head projection + cross-entropy (default); ce: cross-entropy over "
-                         "materialised logits")
-    ap.add_argument("--workload", default=None, help="default llama3 (fused) or ce_llama3 (ce)")
+                         "materialised logits; norm: the RMSNorm that produces H")
+    ap.add_argument("--workload", default=None, help="default llama3 (fused), ce_llama3 (ce), norm_llama3 (norm)")
     ap.add_argument("--cpu-rows", type=int, default=None,
                     help="rows of the oracle sample (default 1024 fused, 8192 ce: 10-20 s of CPU work)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -343,7 +434,7 @@ def main() -> int:
         print(f"bench.py: this build runs on exactly one GPU (asked for {args.gpus}); the multi-GPU "
               "sharding of the path is described, not built.", file=sys.stderr)
         return 2
-    out = run_ce(args) if args.path == "ce" else run_fused(args)
+    out = {"ce": run_ce, "norm": run_norm, "fused": run_fused}[args.path](args)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -1,4 +1,4 @@
-"""ctypes binding of libflce.so (include/flce.h, include/flce_ce.h).  Argument marshalling only: every step
+"""ctypes binding of libflce.so (include/flce.h, include/flce_ce.h, include/flce_norm.h).  Argument marshalling only: every step
 of the computation runs in the library's HIP kernels; torch provides device memory and
 the current stream.
 
@@ -18,8 +18,8 @@ FLCE_OK, FLCE_ERR_INVALID_ARG, FLCE_ERR_ALIGN, FLCE_ERR_WORKSPACE, FLCE_ERR_HIP 
 FLCE_F32, FLCE_BF16, FLCE_F16 = 0, 1, 2
 IGNORE_INDEX = -100
 
-# symbol -> (restype, argtypes), in the order of include/flce.h then include/flce_ce.h
-_P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+# symbol -> (restype, argtypes), in the order of include/flce.h, flce_ce.h, flce_norm.h
+_P, _I64, _I32, _SZ, _F32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
 SIGNATURES = {
     "flce_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I32]),
     "flce_backward_chunks": (_I32, [_I64, _I64, _I64, _I32, _SZ, _P, _P]),
@@ -29,6 +29,9 @@ SIGNATURES = {
     "flce_ce_workspace_bytes": (_SZ, [_I64]),
     "flce_ce_forward": (_I32, [_P, _I64, _P, _I64, _I64, _I32, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
     "flce_ce_backward": (_I32, [_P, _I64, _P, _P, _P, _P, _I64, _I64, _I32, _I64, _P, _I64, _P]),
+    "flce_rmsnorm_workspace_bytes": (_SZ, [_I64, _I64]),
+    "flce_rmsnorm_forward": (_I32, [_P, _P, _I64, _I64, _I32, _F32, _P, _P, _P]),
+    "flce_rmsnorm_backward": (_I32, [_P, _P, _P, _P, _I64, _I64, _I32, _P, _P, _P, _SZ, _P]),
 }
 
 
@@ -195,6 +198,42 @@ def flce_ce_backward(Z, y, lse, n_valid, grad_loss, dZ, ignore_index=IGNORE_INDE
         raise FlceError(st, "flce_ce_backward")
 
 
+# --- RMSNorm of the hidden states (include/flce_norm.h) -------------------------------
+
+
+def flce_rmsnorm_workspace_bytes(N: int, D: int) -> int:
+    return int(lib.flce_rmsnorm_workspace_bytes(int(N), int(D)))
+
+
+def flce_rmsnorm_forward(X, gamma, H, rstd, eps=0.0, stream=None) -> None:
+    """H = X / sqrt(mean(X^2) + eps) * gamma per row; rstd[n] saved for the backward."""
+    N, D = X.shape
+    _check(X, "X")
+    _check(gamma, "gamma", X.dtype, (D,))
+    _check(H, "H", X.dtype, (N, D))
+    _check(rstd, "rstd", torch.float32, (N,))
+    st = lib.flce_rmsnorm_forward(_ptr(X), _ptr(gamma), N, D, dtype_code(X.dtype), float(eps), _ptr(H),
+                                  _ptr(rstd), _stream(stream))
+    if st != FLCE_OK:
+        raise FlceError(st, "flce_rmsnorm_forward")
+
+
+def flce_rmsnorm_backward(X, gamma, rstd, dH, dX, dgamma, workspace, stream=None) -> None:
+    """dX (X's dtype) and dgamma (fp32) of the RMSNorm that produced H, from dH."""
+    N, D = X.shape
+    _check(X, "X")
+    _check(gamma, "gamma", X.dtype, (D,))
+    _check(rstd, "rstd", torch.float32, (N,))
+    _check(dH, "dH", X.dtype, (N, D))
+    _check(dX, "dX", X.dtype, (N, D))
+    _check(dgamma, "dgamma", torch.float32, (D,))
+    _check(workspace, "workspace", torch.uint8)
+    st = lib.flce_rmsnorm_backward(_ptr(X), _ptr(gamma), _ptr(rstd), _ptr(dH), N, D, dtype_code(X.dtype),
+                                   _ptr(dX), _ptr(dgamma), _ptr(workspace), workspace.numel(), _stream(stream))
+    if st != FLCE_OK:
+        raise FlceError(st, "flce_rmsnorm_backward")
+
+
 class FusedLinearCrossEntropy(torch.autograd.Function):
     """loss = mean cross-entropy of (H @ W^T, y) with the fused library.  Saves only the
     per-row lse and N_valid for the backward; dW is returned in fp32."""
@@ -229,3 +268,45 @@ class FusedLinearCrossEntropy(torch.autograd.Function):
 
 def fused_linear_cross_entropy(H, W, y, ignore_index=IGNORE_INDEX):
     return FusedLinearCrossEntropy.apply(H, W, y, ignore_index)
+
+
+class NormLinearCrossEntropy(torch.autograd.Function):
+    """loss = mean cross-entropy of (RMSNorm(X) * gamma @ W^T, y): the final norm, the lm_head
+    and the loss.  Forward saves X, H, rstd, lse and N_valid; the backward's dH feeds the
+    norm's backward directly.  dgamma and dW are returned in fp32 cast to the weights'
+    dtype."""
+
+    @staticmethod
+    def forward(ctx, X, gamma, W, y, eps=0.0, ignore_index=IGNORE_INDEX):
+        N, D = X.shape
+        V = W.shape[0]
+        dev = X.device
+        H = torch.empty_like(X)
+        rstd = torch.empty(N, dtype=torch.float32, device=dev)
+        flce_rmsnorm_forward(X, gamma, H, rstd, eps)
+        ws = torch.empty(flce_workspace_bytes(N, D, V, X.dtype), dtype=torch.uint8, device=dev)
+        loss = torch.empty(1, dtype=torch.float32, device=dev)
+        lse = torch.empty(N, dtype=torch.float32, device=dev)
+        nv = torch.empty(1, dtype=torch.int32, device=dev)
+        status = torch.empty(1, dtype=torch.int32, device=dev)
+        flce_forward(H, W, y, loss, lse, nv, status, ws, ignore_index)
+        ctx.save_for_backward(X, gamma, W, y, H, rstd, lse, nv)
+        ctx.ignore_index = ignore_index
+        return loss[0]
+
+    @staticmethod
+    def backward(ctx, g):
+        X, gamma, W, y, H, rstd, lse, nv = ctx.saved_tensors
+        N, D = X.shape
+        V = W.shape[0]
+        dev = X.device
+        ws = torch.empty(flce_workspace_bytes(N, D, V, X.dtype), dtype=torch.uint8, device=dev)
+        dH = torch.empty_like(H)
+        dW = torch.empty(V, D, dtype=torch.float32, device=dev)
+        gl = g.reshape(1).to(torch.float32).contiguous()
+        flce_backward(H, W, y, lse, nv, gl, dH, dW, ws, ctx.ignore_index)
+        nws = torch.empty(flce_rmsnorm_workspace_bytes(N, D), dtype=torch.uint8, device=dev)
+        dX = torch.empty_like(X)
+        dgamma = torch.empty(D, dtype=torch.float32, device=dev)
+        flce_rmsnorm_backward(X, gamma, rstd, dH, dX, dgamma, nws)
+        return dX, dgamma.to(gamma.dtype), dW.to(W.dtype), None, None, None

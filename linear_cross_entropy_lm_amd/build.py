@@ -11,7 +11,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", "flce.hip"), os.path.join(PKG, "csrc", "ce_logits.hip")]
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("flce.hip", "ce_logits.hip", "rmsnorm.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libflce.so")
 

@@ -433,6 +433,96 @@ def generate_logits(cfg: LogitConfig, threads: int = 8) -> LogitInputs:
     return LogitInputs(cfg, Zt, torch.from_numpy(y).contiguous())
 
 
+# ---------------------------------------------------------------------------------
+# Pre-norm hidden states (the RMSNorm that produces H)
+# ---------------------------------------------------------------------------------
+
+_TENSOR_X, _TENSOR_GAMMA, _TENSOR_DH = 5, 6, 7
+
+
+@dataclass(frozen=True)
+class NormConfig:
+    """X [N, D] ~ N(0, x_std^2) (pre-norm hidden states), gamma [D] ~ 1 + N(0, gamma_std^2)
+    (a trained norm weight near 1), dH [N, D] ~ N(0, dh_std^2) (the gradient of the norm's
+    output; the operation is linear in it, so its scale is free), and eps."""
+
+    name: str
+    N: int
+    D: int
+    dtype: str
+    seed: int
+    x_std: float = 2.0
+    gamma_std: float = 0.1
+    dh_std: float = 1.0
+    eps: float = 1e-5
+
+    def describe(self) -> str:
+        return f"{self.name}: RMSNorm N={self.N}, D={self.D}, {self.dtype}, eps={self.eps:g}"
+
+
+NORM_CONFIGS = {
+    # the final norm before the Llama-3-shaped head: 4 x 4096 tokens, hidden size 4096
+    "norm_llama3": NormConfig("norm_llama3", N=16384, D=4096, dtype="bf16", seed=3001),
+}
+
+
+def norm_case(N: int, D: int, dtype: str = "bf16", seed: int = 9, **kw) -> NormConfig:
+    return NormConfig(f"norm_N{N}_D{D}_{dtype}_s{seed}", N=N, D=D, dtype=dtype, seed=seed, **kw)
+
+
+def _widen(t: torch.Tensor, dtype: str) -> np.ndarray:
+    """Exact fp64 values of a tensor held as fp32 or as 16-bit patterns."""
+    a = t.numpy()
+    if dtype == "f32":
+        return a.astype(np.float64)
+    if dtype == "f16":
+        return a.view(np.float16).astype(np.float64)
+    return bf16_bits_to_f64(a)
+
+
+@dataclass
+class NormInputs:
+    """``X`` [N, D], ``gamma`` [D], ``dH`` [N, D]: fp32, or int16 bit patterns for bf16/f16."""
+
+    cfg: NormConfig
+    X: torch.Tensor
+    gamma: torch.Tensor
+    dH: torch.Tensor
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[self.cfg.dtype]
+
+    def x64(self) -> np.ndarray:
+        return _widen(self.X, self.cfg.dtype)
+
+    def gamma64(self) -> np.ndarray:
+        return _widen(self.gamma, self.cfg.dtype)
+
+    def dh64(self) -> np.ndarray:
+        return _widen(self.dH, self.cfg.dtype)
+
+    def device_tensors(self, device) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+        def dev(t):
+            t = t if self.cfg.dtype == "f32" else t.view(self.torch_dtype)
+            return t.to(device).contiguous()
+        return dev(self.X), dev(self.gamma), dev(self.dH)
+
+
+def generate_norm(cfg: NormConfig, threads: int = 8) -> NormInputs:
+    """Draw X, gamma, dH for ``cfg`` (same exact-arithmetic normals and rounding as
+    ``generate``), each from its own streams."""
+    N, D = cfg.N, cfg.D
+    br = _logit_block_rows(D)
+    X = _normal_rows(N, D, cfg.seed, _TENSOR_X, threads, lambda z: z * cfg.x_std, cfg.dtype, block_rows=br)
+    g = _normal_rows(1, D, cfg.seed, _TENSOR_GAMMA, 1, lambda z: 1.0 + z * cfg.gamma_std, cfg.dtype)
+    dH = _normal_rows(N, D, cfg.seed, _TENSOR_DH, threads, lambda z: z * cfg.dh_std, cfg.dtype, block_rows=br)
+
+    def t(a):
+        return torch.from_numpy(a if cfg.dtype == "f32" else a.view(np.int16)).contiguous()
+    return NormInputs(cfg, t(X), t(g).reshape(D), t(dH))
+
+
 def _exp_neg(x: np.ndarray) -> np.ndarray:
     """exp(-x) for x >= 0 by exact power-of-two reduction and a Taylor series."""
     n = np.floor(x / _LN2)

@@ -48,3 +48,17 @@ def rmsnorm_backward(X: np.ndarray, gamma: np.ndarray, dH: np.ndarray, eps: floa
     dX = (gamma[None, :] * dH) / r[:, None] - X * (s / (d * r ** 3))[:, None]
     dgamma = np.sum(dH * X / r[:, None], axis=0)
     return dict(dX=dX, dgamma=dgamma)
+
+
+def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
+    """x rounded to the storage type ("f32", "bf16" or "f16") with round to nearest even,
+    through fp32 as a kernel computing in fp32 stores it; returned as fp64."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    if dtype == "f32":
+        return f.astype(np.float64)
+    if dtype == "f16":
+        return f.astype(np.float16).astype(np.float64)
+    u = f.view(np.uint32).astype(np.uint64)
+    b = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint32) << 16
+    return b.astype(np.uint32).view(np.float32).astype(np.float64)
+

@@ -8,7 +8,7 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("flce.h", "flce_ce.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("flce.h", "flce_ce.h", "flce_norm.h")]
 
 
 @pytest.fixture(scope="module")
@@ -173,3 +173,43 @@ def test_ce_argument_errors(B):
     assert _ce_bwd(B, ldo=4) == B.FLCE_ERR_INVALID_ARG
     assert _ce_bwd(B, dZ=A16 + 8) == B.FLCE_ERR_ALIGN
     assert _ce_bwd(B, dt=0, ld=6, V=6, ldo=8) == B.FLCE_ERR_ALIGN   # 24-byte fp32 rows
+
+
+# --- RMSNorm of the hidden states ----------------------------------------------------
+
+
+def test_norm_workspace_formula(B):
+    for N, D in [(1, 8), (1000, 4096), (1024, 4096), (16384, 4096), (5000, 12288)]:
+        grid = min(N, 512)
+        groups = -(-grid // 32)
+        assert B.flce_rmsnorm_workspace_bytes(N, D) == _r(grid * D * 4) + _r(groups * D * 4)
+    assert B.flce_rmsnorm_workspace_bytes(0, 8) == 0
+    assert B.flce_rmsnorm_workspace_bytes(8, 16392) == 0
+
+
+# Every call below has at least one argument the library rejects before launching.
+def _n_fwd(B, X=A16, g=A16, N=8, D=64, dt=1, eps=1e-5, H=A16, r=A16):
+    return B.lib.flce_rmsnorm_forward(X, g, N, D, dt, eps, H, r, None)
+
+
+def _n_bwd(B, X=A16, g=A16, r=A16, dH=A16, N=8, D=64, dt=1, dX=A16, dg=A16, ws=A16, wsb=10**8):
+    return B.lib.flce_rmsnorm_backward(X, g, r, dH, N, D, dt, dX, dg, ws, wsb, None)
+
+
+def test_norm_argument_errors(B):
+    assert _n_fwd(B, X=None) == B.FLCE_ERR_INVALID_ARG
+    assert _n_fwd(B, N=0) == B.FLCE_ERR_INVALID_ARG
+    assert _n_fwd(B, dt=3) == B.FLCE_ERR_INVALID_ARG
+    assert _n_fwd(B, eps=-1.0) == B.FLCE_ERR_INVALID_ARG
+    assert _n_fwd(B, eps=float("nan")) == B.FLCE_ERR_INVALID_ARG
+    assert _n_fwd(B, D=16392) == B.FLCE_ERR_INVALID_ARG      # wider than 16384
+    assert _n_fwd(B, dt=0, D=16388) == B.FLCE_ERR_INVALID_ARG
+    assert _n_fwd(B, D=12) == B.FLCE_ERR_ALIGN                # 24-byte bf16 rows
+    assert _n_fwd(B, H=A16 + 4) == B.FLCE_ERR_ALIGN
+    assert _n_fwd(B, r=A16 + 2) == B.FLCE_ERR_ALIGN
+    assert _n_bwd(B, dH=None) == B.FLCE_ERR_INVALID_ARG
+    assert _n_bwd(B, ws=None) == B.FLCE_ERR_INVALID_ARG
+    assert _n_bwd(B, dX=A16 + 8) == B.FLCE_ERR_ALIGN
+    assert _n_bwd(B, dt=0, D=6) == B.FLCE_ERR_ALIGN           # 24-byte fp32 rows
+    assert _n_bwd(B, wsb=100) == B.FLCE_ERR_WORKSPACE
+

@@ -1,0 +1,128 @@
+"""GPU parity of the RMSNorm forward and fused backward (include/flce_norm.h) against the
+fp64 oracle (oracle.rmsnorm_forward / rmsnorm_backward) on the same seeded inputs, and of
+the chain final norm -> lm_head -> cross-entropy through the autograd wrapper.
+
+Tolerances: rstd max relative 1e-5 (an fp32 sum of D squares); H and dX relative
+Frobenius 1e-5 for fp32 outputs, 4e-3 for bf16 (one rounding, 2^-9) and 1e-3 for fp16
+(2^-11); dgamma (fp32, summed over N rows in fp32) relative Frobenius 1e-4.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_cross_entropy_lm_amd import inputs as I
+from flce_run import rel_fro
+
+pytestmark = pytest.mark.gpu
+TOL = {"f32": 1e-5, "bf16": 4e-3, "f16": 1e-3}
+TOL_DGAMMA = 1e-4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from linear_cross_entropy_lm_amd import binding  # noqa: F401  (fails loudly if not built)
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def run_norm(inp, device="cuda:0") -> dict:
+    from linear_cross_entropy_lm_amd import binding as B
+    X, g, dH = inp.device_tensors(device)
+    N, D = X.shape
+    H = torch.full_like(X, float("nan"))
+    rstd = torch.empty(N, dtype=torch.float32, device=device)
+    B.flce_rmsnorm_forward(X, g, H, rstd, inp.cfg.eps)
+    ws = torch.empty(B.flce_rmsnorm_workspace_bytes(N, D), dtype=torch.uint8, device=device)
+    dX = torch.full_like(X, float("nan"))
+    dg = torch.full((D,), float("nan"), dtype=torch.float32, device=device)
+    B.flce_rmsnorm_backward(X, g, rstd, dH, dX, dg, ws)
+    torch.cuda.synchronize()
+    f64 = lambda t: t.float().cpu().double().numpy()  # noqa: E731
+    return dict(H=f64(H), rstd=f64(rstd), dX=f64(dX), dgamma=f64(dg))
+
+
+def check(got, inp):
+    X, g, dH = inp.x64(), inp.gamma64(), inp.dh64()
+    f = oracle.rmsnorm_forward(X, g, inp.cfg.eps)
+    b = oracle.rmsnorm_backward(X, g, dH, inp.cfg.eps)
+    tol = TOL[inp.cfg.dtype]
+    err = dict(rstd=float(np.max(np.abs(got["rstd"] - f["rstd"]) / f["rstd"])),
+               H=rel_fro(got["H"], f["H"]), dX=rel_fro(got["dX"], b["dX"]),
+               dgamma=rel_fro(got["dgamma"], b["dgamma"]))
+    _say("errors", err)
+    assert err["rstd"] <= 1e-5 and err["H"] <= tol and err["dX"] <= tol and err["dgamma"] <= TOL_DGAMMA, err
+
+
+CASES = [
+    ("tiny_f32", I.norm_case(7, 40, "f32", seed=51)),
+    ("ragged_bf16", I.norm_case(300, 1032, "bf16", seed=52, eps=1e-6)),
+    ("ragged_f16", I.norm_case(257, 2056, "f16", seed=53)),
+    ("rows_over_grid_bf16", I.norm_case(1100, 4096, "bf16", seed=54)),     # workgroups take 2 or 3 rows
+    ("nc4_f32", I.norm_case(65, 8192, "f32", seed=55)),
+    ("nc4_partial_bf16", I.norm_case(33, 12288, "bf16", seed=56)),          # 3 of 4 chunks per thread
+    ("nc8_f32", I.norm_case(9, 16384, "f32", seed=57)),
+    ("widest_bf16", I.norm_case(5, 16384, "bf16", seed=58)),
+    ("narrow_rows_bf16", I.norm_case(3000, 8, "bf16", seed=59)),
+    ("eps0_f16", I.norm_case(64, 512, "f16", seed=60, eps=0.0)),
+    ("one_row_f32", I.norm_case(1, 4096, "f32", seed=61)),
+]
+
+
+@pytest.mark.parametrize("name,cfg", CASES, ids=[c[0] for c in CASES])
+def test_norm_parity(name, cfg):
+    _say("case", cfg.describe())
+    inp = I.generate_norm(cfg)
+    check(run_norm(inp), inp)
+
+
+def test_norm_fullsize_llama3():
+    """The final norm before the Llama-3-shaped head: 16384 x 4096 bf16, every element."""
+    cfg = I.NORM_CONFIGS["norm_llama3"]
+    _say("case", cfg.describe())
+    inp = I.generate_norm(cfg)
+    check(run_norm(inp), inp)
+
+
+def test_norm_bitwise_deterministic():
+    inp = I.generate_norm(I.norm_case(2100, 4096, "bf16", seed=62))
+    a, b = run_norm(inp), run_norm(inp)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_norm_lm_head_cross_entropy_chain(dtype):
+    """NormLinearCrossEntropy (norm forward, flce forward; flce backward's dH into the norm
+    backward) against the oracle chain: H = RMSNorm(X) gamma stored in the dtype, the loss
+    and dH of the head, dH stored in the dtype, then the norm's backward."""
+    from linear_cross_entropy_lm_amd import binding as B
+    ncfg = I.norm_case(300, 512, dtype, seed=63)
+    hcfg = I.case(300, 512, 1031, dtype, seed=64)
+    ninp, hinp = I.generate_norm(ncfg), I.generate(hcfg)
+    dev = "cuda:0"
+    X, g, _ = ninp.device_tensors(dev)
+    _, W, y = hinp.device_tensors(dev)
+    Xr = X.clone().requires_grad_(True)
+    gr = g.clone().requires_grad_(True)
+    Wr = W.clone().requires_grad_(True)
+    loss = B.NormLinearCrossEntropy.apply(Xr, gr, Wr, y, ncfg.eps)
+    loss.backward()
+    torch.cuda.synchronize()
+
+    X64, g64, W64, y64 = ninp.x64(), ninp.gamma64(), hinp.w64(), hinp.y64()
+    H = oracle.round_to(oracle.rmsnorm_forward(X64, g64, ncfg.eps)["H"], dtype)
+    ref = oracle.forward_backward(H, W64, y64)
+    dH = oracle.round_to(ref["dH"], dtype)
+    nb = oracle.rmsnorm_backward(X64, g64, dH, ncfg.eps)
+    tol = 1e-5 if dtype == "f32" else 1e-2
+    e_loss = abs(loss.item() - ref["loss"]) / ref["loss"]
+    e_dx = rel_fro(Xr.grad.double().cpu().numpy(), nb["dX"])
+    e_dg = rel_fro(gr.grad.double().cpu().numpy(), nb["dgamma"])
+    e_dw = rel_fro(Wr.grad.double().cpu().numpy(), ref["dW"])
+    _say("chain errors", dict(loss=e_loss, dX=e_dx, dgamma=e_dg, dW=e_dw))
+    assert e_loss <= tol and e_dx <= tol and e_dg <= tol and e_dw <= tol

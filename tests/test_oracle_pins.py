@@ -481,3 +481,15 @@ def test_rmsnorm_finite_differences():
         num_dg[j] = (L(X, gp) - L(X, gm)) / (2 * h)
     assert np.linalg.norm(num_dX - b["dX"]) <= 1e-7 * np.linalg.norm(b["dX"])
     assert np.linalg.norm(num_dg - b["dgamma"]) <= 1e-7 * np.linalg.norm(b["dgamma"])
+
+
+def test_round_to_matches_torch_casts():
+    """The storage rounding used for chained cases equals torch's own fp32 -> bf16 / fp16
+    casts (round to nearest even)."""
+    rng = np.random.default_rng(12)
+    x = np.concatenate([rng.normal(0, 3, 5000), rng.normal(0, 1e-3, 1000), [0.0, -0.0, 1.0, 65504.0]])
+    f32 = x.astype(np.float32)
+    for dt, tdt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
+        ref = torch.from_numpy(f32).to(tdt).to(torch.float64).numpy()
+        assert np.array_equal(oracle.round_to(x, dt), ref)
+    assert np.array_equal(oracle.round_to(x, "f32"), f32.astype(np.float64))
