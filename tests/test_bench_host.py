@@ -1,0 +1,72 @@
+"""Host-side checks of bench.py's arithmetic (no GPU): the algorithmic byte counts behind
+the HBM rooflines, the counter-record summariser and its calibration scaling, and that a
+traffic record taken on another kernel source is ignored."""
+import csv
+import json
+import os
+
+import pytest
+
+import bench
+
+
+def test_ce_row_bytes():
+    # forward: the row (V es) + label (8) + lse (4) + loss term (8) + flag (4)
+    # backward: the row read and written (2 V es) + label (8) + lse (4)
+    assert bench.ce_row_bytes(128256, 2) == (128256 * 2 + 24, 4 * 128256 + 12)
+    assert bench.ce_row_bytes(7, 4) == (7 * 4 + 24, 2 * 7 * 4 + 12)
+
+
+def test_norm_bytes():
+    N, D, es, grid = 16384, 4096, 2, 512
+    fwd, bwd = bench.norm_bytes(N, D, es, grid)
+    assert fwd == 2 * N * D * es + 4 * N + D * es
+    groups = 16  # 512 partial rows summed 32 at a time
+    assert bwd == 3 * N * D * es + 4 * N + D * es + 2 * grid * D * 4 + 2 * groups * D * 4 + D * 4
+    assert bench.norm_bytes(3, 8, 4, 3)[1] == 3 * 3 * 8 * 4 + 12 + 32 + 2 * 3 * 8 * 4 + 2 * 1 * 8 * 4 + 32
+
+
+def _write_counters(path, kernel, counter, values):
+    os.makedirs(path, exist_ok=True)
+    with open(os.path.join(path, "x_counter_collection.csv"), "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for i, v in enumerate(values):
+            # two rows per dispatch (per-XCD style pieces) that the reader must add up
+            w.writerow([i, f"void {kernel}(int)", counter, v / 2])
+            w.writerow([i, f"void {kernel}(int)", counter, v / 2])
+        w.writerow([99, "other_kernel", counter, 1e9])
+
+
+@pytest.mark.parametrize("path", sorted(bench.PATHS))
+def test_summarize_counters_scales_by_the_copy(tmp_path, monkeypatch, path):
+    kernel = bench.PATHS[path][0]
+    rec_file = tmp_path / "rec.json"
+    monkeypatch.setitem(bench.PATHS, path, (kernel, "w", str(rec_file), bench.PATHS[path][3]))
+    root = tmp_path / "cnt"
+    copy = 1 << 30
+    _write_counters(root / "F", kernel, "FETCH_SIZE", [1000.0, 3000.0])
+    _write_counters(root / "W", kernel, "WRITE_SIZE", [500.0, 500.0])
+    # a 1 GiB copy whose counters read half the fetched bytes and all the written bytes
+    _write_counters(root / "FC", "__amd_rocclr_copyBuffer", "FETCH_SIZE", [copy / 2048.0])
+    _write_counters(root / "WC", "__amd_rocclr_copyBuffer", "WRITE_SIZE", [copy / 1024.0])
+    rec = bench.summarize_counters(str(root), copy, path)
+    assert rec["fetch_kib_per_launch"] == 2000.0 and rec["write_kib_per_launch"] == 500.0
+    assert rec["fetch_factor"] == pytest.approx(2.0) and rec["write_factor"] == pytest.approx(1.0)
+    assert rec["hbm_bytes_per_launch"] == pytest.approx(2000.0 * 1024 * 2 + 500.0 * 1024)
+    assert json.loads(rec_file.read_text())["source_digest"] == bench.source_digest(path)
+    assert bench.load_traffic(path) == pytest.approx(rec["hbm_bytes_per_launch"])
+
+
+def test_traffic_record_of_another_source_is_ignored(tmp_path, monkeypatch):
+    rec_file = tmp_path / "rec.json"
+    rec_file.write_text(json.dumps({"source_digest": "0" * 16, "hbm_bytes_per_launch": 1.0}))
+    kernel, wl, _, src = bench.PATHS["fused"]
+    monkeypatch.setitem(bench.PATHS, "fused", (kernel, wl, str(rec_file), src))
+    assert bench.load_traffic("fused") is None
+
+
+def test_more_than_one_gpu_is_refused(capsys, monkeypatch):
+    monkeypatch.setattr("sys.argv", ["bench.py", "--gpus", "2"])
+    assert bench.main() == 2
+    assert "one GPU" in capsys.readouterr().err
