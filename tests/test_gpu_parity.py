@@ -42,6 +42,9 @@ CASES = [
     ("ragged_f16", I.case(300, 512, 1031, "f16", seed=17)),
     ("raggedD_f16", I.case(513, 264, 2500, "f16", seed=18, ignore_frac=0.2)),
     ("zipf_f16", I.case(640, 256, 4099, "f16", seed=19, label_dist="zipf")),
+    # one row past 16 token tiles (two uneven token chunks) and a ragged 32003-row
+    # vocabulary over four vocabulary chunks
+    ("odd_NV_bf16", I.case(4097, 256, 32003, "bf16", seed=20)),
 ]
 
 
