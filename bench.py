@@ -53,9 +53,19 @@ PATHS = {
 }
 
 
+def code_digest(text: str) -> str:
+    """Digest of a C++/HIP source's code: comments removed and whitespace collapsed, so an
+    edit to comments alone does not make a counter record stale."""
+    import re
+    code = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    code = re.sub(r"//[^\n]*", " ", code)
+    code = " ".join(code.split())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
+
+
 def source_digest(path: str = "fused") -> str:
-    with open(PATHS[path][3], "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    with open(PATHS[path][3], encoding="utf-8") as f:
+        return code_digest(f.read())
 
 
 def load_traffic(path: str = "fused"):
@@ -128,6 +138,24 @@ def summarize_counters(root: str, copy_bytes: int, path: str = "fused") -> dict:
     return rec
 
 
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def device_info() -> dict:
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+            "memory_gb": round(p.total_memory / 1e9, 1)}
+
+
 def cpu_baseline(inp, rows: int) -> dict:
     import numpy as np
     import oracle
@@ -143,7 +171,7 @@ def cpu_baseline(inp, rows: int) -> dict:
     oracle.forward_backward(H, W, y)
     dt = time.perf_counter() - t0
     del W
-    return {"value": rows / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+    return {"value": rows / dt, "unit": "tokens/s", "cores": int(cores), "cpu_model": host_cpu_model(), "kind": "oracle",
             "sample": f"first {rows} of {inp.cfg.N} token rows, full V={inp.cfg.V}, D={inp.cfg.D}: "
                       f"fp64 loss, lse, dH and dW in {dt:.1f} s",
             "seconds": dt, "fp64_gflops": 6.0 * rows * inp.cfg.V * inp.cfg.D / dt / 1e9}
@@ -162,7 +190,7 @@ def cpu_baseline_ce(inp, rows: int) -> dict:
     t0 = time.perf_counter()
     oracle.ce_from_logits(Z, y)
     dt = time.perf_counter() - t0
-    return {"value": rows / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+    return {"value": rows / dt, "unit": "tokens/s", "cores": int(cores), "cpu_model": host_cpu_model(), "kind": "oracle",
             "sample": f"first {rows} of {inp.cfg.N} logit rows, full V={inp.cfg.V}: fp64 loss, lse and dZ "
                       f"in {dt:.1f} s", "seconds": dt}
 
@@ -170,7 +198,7 @@ def cpu_baseline_ce(inp, rows: int) -> dict:
 def _common(args, metric, value, ms, dtype, data, config):
     return {"metric": metric, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "dtype": dtype, "data": data, "config": config}
+            "vs_baseline": None, "dtype": dtype, "data": data, "config": config, "device": device_info()}
 
 
 def run_fused(args) -> dict:
@@ -309,7 +337,7 @@ def cpu_baseline_norm(inp) -> dict:
     oracle.rmsnorm_forward(X, g, inp.cfg.eps)
     oracle.rmsnorm_backward(X, g, dH, inp.cfg.eps)
     dt = time.perf_counter() - t0
-    return {"value": inp.cfg.N / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+    return {"value": inp.cfg.N / dt, "unit": "tokens/s", "cores": int(cores), "cpu_model": host_cpu_model(), "kind": "oracle",
             "sample": f"all {inp.cfg.N} rows, D={inp.cfg.D}: fp64 H, rstd, dX and dgamma in {dt:.1f} s",
             "seconds": dt}
 

@@ -11,8 +11,8 @@
 //     workgroup (eight wave64s, two per SIMD, each owning 128 x 64 as 4 x 2 MFMA blocks
 //     of 32 x 32), K staged through LDS in 128-byte slices, double buffered, one barrier
 //     per slice.  Workgroups are persistent: each walks a list of tiles with one
-//     continuous load pipeline.  bf16 uses v_mfma_f32_32x32x16_bf16; fp32 uses
-//     v_mfma_f32_32x32x2_f32.
+//     continuous load pipeline.  bf16 uses v_mfma_f32_32x32x16_bf16, fp16
+//     v_mfma_f32_32x32x16_f16, fp32 v_mfma_f32_32x32x2_f32.
 //   * Operands move HBM -> LDS with direct DMA loads (no register staging), into
 //     unpadded LDS rows whose 16-byte chunks are XOR-swizzled so fragment reads are free
 //     of bank conflicts.

@@ -70,3 +70,11 @@ def test_more_than_one_gpu_is_refused(capsys, monkeypatch):
     monkeypatch.setattr("sys.argv", ["bench.py", "--gpus", "2"])
     assert bench.main() == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_code_digest_ignores_comments_only():
+    src = "int f(int x) {  // doubles x\n  return 2 * x; /* twice */ }\n"
+    same = "// header\nint f(int x) {\n  return 2 * x;\n}\n"
+    other = "int f(int x) { return 3 * x; }\n"
+    assert bench.code_digest(src) == bench.code_digest(same)
+    assert bench.code_digest(src) != bench.code_digest(other)
