@@ -6,6 +6,10 @@
 One step = flce_forward + flce_backward over one batch of synthetic input already
 resident in HBM (loss, lse, dH, dW all produced).  Prints one JSON line.
 
+--path single measures flce_forward_backward with the single-pass workspace (the logits
+computed once, 6·N·V·D flops; scratch about 25% of the 16-bit N x V logit bytes, above
+the 5% the default path keeps): same workload and credit (8·N·V·D) as the default line.
+
 --path norm measures the RMSNorm that produces H (include/flce_norm.h): one step =
 flce_rmsnorm_forward + flce_rmsnorm_backward at 16384 x 4096 bf16; its roofline is the
 backward call (rms_bwd and its two small dgamma passes) against the HBM peak.
@@ -39,6 +43,7 @@ sys.path.insert(0, ROOT)
 METRIC = "fused linear-CE fwd+bwd tokens/s at N=16384,D=4096,V=128256; % bf16 MFMA peak"
 METRIC_CE = "cross-entropy over materialised logits fwd+bwd tokens/s at N=16384,V=128256; % HBM peak"
 METRIC_NORM = "RMSNorm fwd+fused bwd tokens/s at N=16384,D=4096; % HBM peak"
+METRIC_SINGLE = "fused linear-CE fwd+bwd in one call, single pass, tokens/s at N=16384,D=4096,V=128256; % bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "linear_cross_entropy_lm_amd", "csrc")
@@ -48,6 +53,8 @@ PATHS = {
               os.path.join(CSRC, "flce.hip")),
     "ce": ("ce_rows_bwd", "ce_llama3", os.path.join(ROOT, "profiles", "ce_rows_bwd_ce_llama3_traffic.json"),
            os.path.join(CSRC, "ce_logits.hip")),
+    "single": ("fwd_tiles", "llama3", os.path.join(ROOT, "profiles", "fwd_tiles_keep_llama3_traffic.json"),
+               os.path.join(CSRC, "flce.hip")),
     "norm": ("rms_bwd", "norm_llama3", os.path.join(ROOT, "profiles", "rms_bwd_norm_llama3_traffic.json"),
              os.path.join(CSRC, "rmsnorm.hip")),
 }
@@ -266,6 +273,64 @@ def run_fused(args) -> dict:
     return out
 
 
+def run_single(args) -> dict:
+    import torch
+    from linear_cross_entropy_lm_amd import binding as B
+    from linear_cross_entropy_lm_amd import inputs as I
+    from linear_cross_entropy_lm_amd.scratch import scratch_fraction
+
+    cfg = I.CONFIGS[args.workload or "llama3"]
+    inp = I.generate(cfg)
+    dev = "cuda:0"
+    H, W, y = inp.device_tensors(dev)
+    N, D, V = cfg.N, cfg.D, cfg.V
+    ws_bytes = B.flce_forward_backward_workspace_bytes(N, D, V, H.dtype)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    nv = torch.empty(1, dtype=torch.int32, device=dev)
+    st = torch.empty(1, dtype=torch.int32, device=dev)
+    dH = torch.empty_like(H)
+    dW = torch.empty(V, D, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+            ev[1].record(stream)
+        B.flce_forward_backward(H, W, y, None, loss, lse, nv, st, dH, dW, ws, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    ms, _, step_ms, peak_delta = _time_steps(args, step, stream)
+    if int(st.item()) != 0:
+        raise RuntimeError("dev_status reports invalid labels")
+    flop_credit = 8.0 * N * V * D
+    out = _common(args, METRIC_SINGLE, N / (ms * 1e-3), ms, cfg.dtype,
+                  "synthetic: seeded Gaussian H with unit-RMS rows, W ~ N(0, 0.02^2), uniform labels, "
+                  f"{cfg.n_ignored} ignore_index rows",
+                  {"workload": f"{cfg.name}-shaped lm_head + cross-entropy, fwd+bwd in one call (single pass)",
+                   "N": N, "D": D, "V": V, "batch": cfg.batch, "seq_len": cfg.seq, "parallelism": "single GPU"})
+    out.update({
+        "mfma_peak_frac": flop_credit / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+        "executed_flop_frac": 0.75 * flop_credit / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+        "step_ms_median": step_ms[len(step_ms) // 2],
+        "step_ms_min": step_ms[0],
+        "step_ms_max": step_ms[-1],
+        "scratch_bytes": ws_bytes,
+        "torch_peak_alloc_delta_bytes": int(peak_delta),
+        "scratch_frac_of_unfused_logits": scratch_fraction(ws_bytes, N, V),
+        "loss": float(loss.item()),
+        "roofline": {"kernel": "whole call (6 N V D executed)", "bound": "mfma",
+                     "achieved": 6.0 * N * V * D / (ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": 6.0 * N * V * D / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "traffic": None},
+        "cpu_baseline": None,
+    })
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows or 1024)
+    return out
+
+
 def run_ce(args) -> dict:
     import torch
     from linear_cross_entropy_lm_amd import binding as B
@@ -433,8 +498,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--path", choices=sorted(PATHS), default="fused",
-                    help="fused: lm_head projection + cross-entropy (default); ce: cross-entropy over "
-                         "materialised logits; norm: the RMSNorm that produces H")
+                    help="fused: lm_head projection + cross-entropy (default); single: the same in one "
+                         "call without logit recompute (25%% scratch); ce: cross-entropy over materialised "
+                         "logits; norm: the RMSNorm that produces H")
     ap.add_argument("--workload", default=None, help="default llama3 (fused), ce_llama3 (ce), norm_llama3 (norm)")
     ap.add_argument("--cpu-rows", type=int, default=None,
                     help="rows of the oracle sample (default 1024 fused, 8192 ce: 10-20 s of CPU work)")
@@ -462,7 +528,7 @@ def main() -> int:
         print(f"bench.py: this build runs on exactly one GPU (asked for {args.gpus}); the multi-GPU "
               "sharding of the path is described, not built.", file=sys.stderr)
         return 2
-    out = {"ce": run_ce, "norm": run_norm, "fused": run_fused}[args.path](args)
+    out = {"ce": run_ce, "norm": run_norm, "single": run_single, "fused": run_fused}[args.path](args)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -134,6 +134,40 @@ flce_status flce_backward(const void* H, const void* W, const int64_t* y, const 
                           int64_t V, int dtype, int64_t ignore_index, void* dH, float* dW,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Single-pass workspace: the bytes flce_forward_backward needs to run without recomputing
+ * the logits.  Token chunks of T = min(N, 4096) rows (rounded up to 256) keep, for the
+ * whole vocabulary, p~ = exp(z - m) in the input type (T x V' elements, V' = V rounded up
+ * to 256) and the maxima m of each 128-row half tile in fp32 (T x V'/128), plus a few MB
+ * of per-row and per-block terms: about T V' es + 4 T V'/128 bytes (1.07 GB, 25% of the
+ * 16-bit N x V logit bytes, at N = 16384, V = 128256, bf16).  0 for invalid sizes.
+ */
+size_t flce_forward_backward_workspace_bytes(int64_t N, int64_t D, int64_t V, int dtype);
+
+/*
+ * Forward and backward in one call: loss, lse[N], n_valid, dev_status as flce_forward and
+ * dH, dW (for the upstream gradient *grad_loss, NULL meaning 1) as flce_backward.
+ *
+ * "Unsloth Architecture: 5x Faster LLM Training via Triton", pillar 1 and its numpy walk
+ * through, computes the loss and the hidden-state gradient of a token chunk in one pass
+ * over its logits; "Arquitectura interna de Unsloth y optimización en Triton", section 3,
+ * backpropagates into H and W directly.  With workspace_bytes >=
+ * flce_forward_backward_workspace_bytes(...), each token chunk's logits are computed once
+ * (6 N V D flops in all): the logit GEMM keeps p~ and m, the chunk's lse is combined,
+ * p~ becomes dz in place, and dH (over the whole vocabulary at once) and dW are contracted
+ * from it.  With a smaller workspace (at least flce_workspace_bytes) the call runs
+ * flce_forward then flce_backward (8 N V D flops, the logits recomputed).
+ *
+ * Conventions, alignment, errors and determinism as flce_forward / flce_backward; results
+ * of the two schedules agree within rounding (the single pass rounds p~ to the input type
+ * before scaling it to dz).
+ */
+flce_status flce_forward_backward(const void* H, const void* W, const int64_t* y, int64_t N, int64_t D,
+                                  int64_t V, int dtype, int64_t ignore_index, const float* grad_loss,
+                                  float* loss, float* lse, int32_t* n_valid, int32_t* dev_status,
+                                  void* dH, float* dW, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* flce_status_string(int status);
 

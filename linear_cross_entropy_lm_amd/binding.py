@@ -25,6 +25,9 @@ SIGNATURES = {
     "flce_backward_chunks": (_I32, [_I64, _I64, _I64, _I32, _SZ, _P, _P]),
     "flce_forward": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I32, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
     "flce_backward": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I64, _P, _P, _P, _SZ, _P]),
+    "flce_forward_backward_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I32]),
+    "flce_forward_backward": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I32, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
+                                     _P]),
     "flce_status_string": (ctypes.c_char_p, [_I32]),
     "flce_ce_workspace_bytes": (_SZ, [_I64]),
     "flce_ce_forward": (_I32, [_P, _I64, _P, _I64, _I64, _I32, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -143,6 +146,36 @@ def flce_backward(H, W, y, lse, n_valid, grad_loss, dH, dW, workspace, ignore_in
                            _ptr(workspace), workspace.numel(), _stream(stream))
     if st != FLCE_OK:
         raise FlceError(st, "flce_backward")
+
+
+def flce_forward_backward_workspace_bytes(N: int, D: int, V: int, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    return int(lib.flce_forward_backward_workspace_bytes(N, D, V, code))
+
+
+def flce_forward_backward(H, W, y, grad_loss, loss, lse, n_valid, dev_status, dH, dW, workspace,
+                          ignore_index=IGNORE_INDEX, stream=None) -> None:
+    """Forward and backward in one call; the single-pass schedule when ``workspace`` holds
+    flce_forward_backward_workspace_bytes, else forward then the recomputing backward."""
+    N, D = H.shape
+    V = W.shape[0]
+    _check(H, "H")
+    _check(W, "W", H.dtype, (V, D))
+    _check(y, "y", torch.int64, (N,))
+    if grad_loss is not None:
+        _check(grad_loss, "grad_loss", torch.float32, (1,))
+    _check(loss, "loss", torch.float32, (1,))
+    _check(lse, "lse", torch.float32, (N,))
+    _check(n_valid, "n_valid", torch.int32, (1,))
+    _check(dev_status, "dev_status", torch.int32, (1,))
+    _check(dH, "dH", H.dtype, (N, D))
+    _check(dW, "dW", torch.float32, (V, D))
+    _check(workspace, "workspace", torch.uint8)
+    st = lib.flce_forward_backward(_ptr(H), _ptr(W), _ptr(y), N, D, V, dtype_code(H.dtype), ignore_index,
+                                   _ptr(grad_loss), _ptr(loss), _ptr(lse), _ptr(n_valid), _ptr(dev_status),
+                                   _ptr(dH), _ptr(dW), _ptr(workspace), workspace.numel(), _stream(stream))
+    if st != FLCE_OK:
+        raise FlceError(st, "flce_forward_backward")
 
 
 # --- cross-entropy over materialised logits (include/flce_ce.h) ----------------------

@@ -54,6 +54,7 @@ typedef u32 u32x2 __attribute__((ext_vector_type(2)));
 typedef u32 u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kWaves = 8;                          // wave64s per workgroup, two per SIMD
@@ -544,6 +545,9 @@ template <typename T> __device__ __forceinline__ int even_slices(int K) {
 // Forward
 // ---------------------------------------------------------------------------------
 
+// Four consecutive values stored in the element type (defined with the backward epilogues).
+template <typename T> __device__ __forceinline__ void store4(T* p, const float (&d)[4]);
+
 // LDS past the two GEMM stages, for the cross-wave (max, sum-exp) merge.
 constexpr int kRedBytes = 2 * kTile * (int)sizeof(float2);
 
@@ -552,13 +556,29 @@ constexpr int kRedBytes = 2 * kTile * (int)sizeof(float2);
 // token's running (max, sum-exp) across those tiles (thread t < 256 holds token 256 nt + t)
 // and writes one partial per token to part[sp][n].  The label logit of a valid row is
 // written by the one lane whose tile holds the label.
-template <typename T>
+//
+// KEEP (the single-pass schedule): the workgroup also keeps the exponentials it computes.
+// For each token and each half tile of 128 vocabulary rows (one wave's rows) it takes the
+// maximum m over that half, writes p~ = exp(z - m) for the half's rows to
+// keep[n][v] (zero past V) and m to mkeep[n][v / 128]; then exp(z - lse) = p~ exp(m - lse)
+// once lse is known.  p~ lies in (0, 1], so storing it in the input type costs one
+// rounding of relative size 2^-8 (bf16), like the dz slab; a logit stored instead would
+// carry an absolute error of |z| 2^-8 into exp.  The (nt, sp) grid is then walked in the
+// order of tile_rc, so each XCD's 32 workgroups form a 4 x 8 block of (split, token tile).
+template <typename T, bool KEEP>
 __global__ __launch_bounds__(kThreads, 1) void fwd_tiles(const T* __restrict__ H, const T* __restrict__ W,
                                                           const int64_t* __restrict__ y, int N, int D, int V,
                                                           int n_tiles_n, int splits, float2* __restrict__ part,
-                                                          float* __restrict__ zlab) {
+                                                          float* __restrict__ zlab, T* __restrict__ keep, int ld_keep,
+                                                          float* __restrict__ mkeep, int ld_mkeep) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes + kRedBytes];
-  const int nt = blockIdx.x % n_tiles_n, sp = blockIdx.x / n_tiles_n;
+  int nt, sp;
+  if constexpr (KEEP) {
+    tile_rc((int)blockIdx.x, splits, n_tiles_n, sp, nt);
+  } else {
+    nt = blockIdx.x % n_tiles_n;
+    sp = blockIdx.x / n_tiles_n;
+  }
   const int n_vt = (V + kTile - 1) / kTile;
   const int count = (n_vt - sp + splits - 1) / splits;
   const int n0 = nt * kTile;
@@ -590,6 +610,54 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles(const T* __restrict__ H
     for (int j = 0; j < kBN; ++j) {
       const int n = n0 + wn * kWaveN + 32 * j + lr;
       float m = -__builtin_inff();
+      if constexpr (KEEP) {
+        // Maximum over the wave's 128 rows first (this lane's 64 and lane ^ 32's), then the
+        // exponentials against it, kept and summed.
+        if (full) {
+#pragma unroll
+          for (int ii = 0; ii < kBM; ++ii)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[ii][j][r]);
+        } else {
+#pragma unroll
+          for (int ii = 0; ii < kBM; ++ii)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (32 * ii + 8 * (r >> 2) + (r & 3) < vlim) m = fmaxf(m, acc[ii][j][r]);
+        }
+        m = fmaxf(m, __shfl_xor(m, 32));
+        const float mb = (m == -__builtin_inff() ? 0.f : m) * kLog2e;
+        T* out = keep + (int64_t)(n0 + wn * kWaveN + 32 * j + lr) * ld_keep + vbase;
+        float sum = 0.f;
+#pragma unroll
+        for (int ii = 0; ii < kBM; ++ii)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float d[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float p = hw_exp2(__builtin_fmaf(acc[ii][j][4 * q + e], kLog2e, -mb));
+              d[e] = full || 32 * ii + 8 * q + e < vlim ? p : 0.f;
+              sum += d[e];
+            }
+            store4<T>(out + 32 * ii + 8 * q, d);
+          }
+        sum += __shfl_xor(sum, 32);
+        if (lh == 0) mkeep[(int64_t)(n0 + wn * kWaveN + 32 * j + lr) * ld_mkeep + (v0 + wm * kWaveM) / 128] = m;
+        const int64_t rel = lab[j] - vbase;
+        if (n < N && rel >= 0 && rel < kWaveM && (rel & 4) == 0) {
+          float zl = 0.f;
+#pragma unroll
+          for (int ii = 0; ii < kBM; ++ii)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (rel == 32 * ii + 8 * (r >> 2) + (r & 3)) zl = acc[ii][j][r];
+          zlab[n] = zl;
+        }
+        mrow[j] = m;
+        srow[j] = sum;
+        continue;
+      }
       if (full) {
 #pragma unroll
         for (int ii = 0; ii < kBM; ++ii)
@@ -1007,6 +1075,138 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dw(const T* __restrict__ slab
 }
 
 // ---------------------------------------------------------------------------------
+// Single-pass schedule (forward and backward in one call, no logit recompute)
+// ---------------------------------------------------------------------------------
+
+// Labels of 256 rows: count of valid rows and the bad-label flag (N_valid is needed before
+// any token chunk's gradient is formed).
+__global__ __launch_bounds__(256) void label_blocks(const int64_t* __restrict__ y, int N, int V, int64_t ignore_index,
+                                                   int* __restrict__ blk_cnt, int* __restrict__ blk_bad) {
+  __shared__ int sc[256], sb[256];
+  const int t = threadIdx.x, n = blockIdx.x * 256 + t;
+  int c = 0, b = 0;
+  if (n < N) {
+    const int64_t l = y[n];
+    if (l != ignore_index) {
+      if (l >= 0 && l < V)
+        c = 1;
+      else
+        b = 1;
+    }
+  }
+  sc[t] = c;
+  sb[t] = b;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (t < w) {
+      sc[t] += sc[t + w];
+      sb[t] |= sb[t + w];
+    }
+    __syncthreads();
+  }
+  if (t == 0) {
+    blk_cnt[blockIdx.x] = sc[0];
+    blk_bad[blockIdx.x] = sb[0];
+  }
+}
+
+__global__ __launch_bounds__(256) void label_total(const int* __restrict__ blk_cnt, int nblk, int32_t* __restrict__ n_valid) {
+  __shared__ int sc[256];
+  const int t = threadIdx.x;
+  int c = 0;
+  for (int i = t; i < nblk; i += 256) c += blk_cnt[i];
+  sc[t] = c;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (t < w) sc[t] += sc[t + w];
+    __syncthreads();
+  }
+  if (t == 0) *n_valid = sc[0];
+}
+
+// The kept exponentials of one token chunk become the dz slab, in place:
+//   slab[n][v] = sign(c) a p~[n][v] exp(m - lse) (- sign(c) a at the label)
+//              = p~ * copysign(2^(m log2(e) - e2[n]), c)  (- coef[n] at the label),
+// with m = mkeep[n][v / 128] and e2, coef, lab from bwd_prep (a = |c|, or 2^14 for fp16).
+// Rows [0, rows) of the chunk; each thread one 16-byte chunk of a row, 512 per piece,
+// consecutive workgroups on consecutive pieces.
+constexpr int kDzThreads = 512;
+
+template <typename T> struct Pack16;
+template <> struct Pack16<u16> {
+  static constexpr int K = 8;
+  static __device__ __forceinline__ void decode(const u32x4& w, float (&z)[K]) {
+    const f32x8 f = __builtin_convertvector(__builtin_bit_cast(bf16x8, w), f32x8);
+#pragma unroll
+    for (int e = 0; e < K; ++e) z[e] = f[e];
+  }
+  static __device__ __forceinline__ u32x4 encode(const float (&d)[K]) {
+    f32x8 f;
+#pragma unroll
+    for (int e = 0; e < K; ++e) f[e] = d[e];
+    return __builtin_bit_cast(u32x4, __builtin_convertvector(f, bf16x8));
+  }
+};
+template <> struct Pack16<h16> {
+  static constexpr int K = 8;
+  static __device__ __forceinline__ void decode(const u32x4& w, float (&z)[K]) {
+    const f32x8 f = __builtin_convertvector(__builtin_bit_cast(f16x8, w), f32x8);
+#pragma unroll
+    for (int e = 0; e < K; ++e) z[e] = f[e];
+  }
+  static __device__ __forceinline__ u32x4 encode(const float (&d)[K]) {
+    f32x8 f;
+#pragma unroll
+    for (int e = 0; e < K; ++e) f[e] = d[e];
+    return __builtin_bit_cast(u32x4, __builtin_convertvector(f, f16x8));
+  }
+};
+template <> struct Pack16<float> {
+  static constexpr int K = 4;
+  static __device__ __forceinline__ void decode(const u32x4& w, float (&z)[K]) {
+    const f32x4 f = __builtin_bit_cast(f32x4, w);
+#pragma unroll
+    for (int e = 0; e < K; ++e) z[e] = f[e];
+  }
+  static __device__ __forceinline__ u32x4 encode(const float (&d)[K]) {
+    f32x4 f;
+#pragma unroll
+    for (int e = 0; e < K; ++e) f[e] = d[e];
+    return __builtin_bit_cast(u32x4, f);
+  }
+};
+
+template <typename T>
+__global__ __launch_bounds__(kDzThreads) void keep_to_dz(T* __restrict__ slab, int ld_slab, int rows,
+                                                         const float* __restrict__ mkeep, int ld_mkeep,
+                                                         const float* __restrict__ e2, const float* __restrict__ coef,
+                                                         const int* __restrict__ lab, int64_t pieces, int P) {
+  using F = Pack16<T>;
+  constexpr int K = F::K;
+  const int row_chunks = ld_slab / K;
+  for (int64_t q = blockIdx.x; q < pieces; q += gridDim.x) {
+    const int n = (int)(q / P);
+    const int ch = (int)(q - (int64_t)n * P) * kDzThreads + (int)threadIdx.x;
+    if (n >= rows || ch >= row_chunks) continue;
+    const int v0 = ch * K;
+    const float c = coef[n];
+    const float f = __builtin_copysignf(hw_exp2(__builtin_fmaf(mkeep[(int64_t)n * ld_mkeep + v0 / 128], kLog2e, -e2[n])), c);
+    T* p = slab + (int64_t)n * ld_slab + v0;
+    float z[K], d[K];
+    F::decode(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)), z);
+#pragma unroll
+    for (int e = 0; e < K; ++e) d[e] = z[e] * f;
+    const int rel = lab[n] - v0;
+    if (rel >= 0 && rel < K) {
+#pragma unroll
+      for (int e = 0; e < K; ++e)
+        if (e == rel) d[e] -= c;
+    }
+    *reinterpret_cast<u32x4*>(p) = F::encode(d);
+  }
+}
+
+// ---------------------------------------------------------------------------------
 // Host side: argument checks, workspace carving, launch sequences.
 // ---------------------------------------------------------------------------------
 
@@ -1137,8 +1337,8 @@ flce_status forward_impl(const T* H, const T* W, const int64_t* y, int N, int D,
   int* bbad = reinterpret_cast<int*>(ws + L.bbad);
   const int ntn = (int)ceil_div(N, kTile);
   (void)hipGetLastError();
-  fwd_tiles<T><<<dim3((unsigned)ntn * (unsigned)L.splits), dim3(kThreads), 0, s>>>(H, W, y, N, D, V, ntn, L.splits,
-                                                                                   part, zlab);
+  fwd_tiles<T, false><<<dim3((unsigned)ntn * (unsigned)L.splits), dim3(kThreads), 0, s>>>(
+      H, W, y, N, D, V, ntn, L.splits, part, zlab, nullptr, 0, nullptr, 0);
   fwd_combine<<<dim3(L.nblk), dim3(256), 0, s>>>(part, L.splits, zlab, y, N, V, ignore_index, lse, bloss, bcnt, bbad);
   fwd_finalize<<<dim3(1), dim3(256), 0, s>>>(bloss, bcnt, bbad, L.nblk, loss, n_valid, dev_status);
   return launched();
@@ -1201,6 +1401,117 @@ flce_status backward_impl(const T* H, const T* W, const int64_t* y, const float*
         bwd_dw<T, false><<<gw, blk, 0, s>>>(slab, ld_slab, H, D, t0c, tc_act, v0c, vc_act, n_td, dW, oscale);
     }
   }
+  return launched();
+}
+
+// Single-pass workspace: token chunks of tc rows (min(N, 4096) rounded up to 256) keep
+// their exponentials for the whole vocabulary: keep [tc][ld] in the input type, ld = V
+// rounded up to 256, and mkeep [tc][ld / 128] fp32; plus the forward partials of one chunk,
+// per-row terms of one chunk, and block sums over all N rows.
+struct SpLayout {
+  int64_t tc, ld, ld_m;
+  int splits, nblk;
+  size_t lcnt, lbad, nv, part, zlab, bloss, bcnt, bbad, e2, coef, lab, oscale, mkeep, keep, total;
+};
+
+SpLayout sp_layout(int64_t N, int64_t V, int dtype) {
+  SpLayout L;
+  L.tc = round_up(N < kDefaultTokenChunk ? N : kDefaultTokenChunk, kTile);
+  L.ld = round_up(V, kTile);
+  L.ld_m = L.ld / 128;
+  const int64_t ntn = L.tc / kTile, n_vt = L.ld / kTile;
+  int64_t sp = kPersistentWGs / ntn;
+  L.splits = (int)(sp < 1 ? 1 : (sp > n_vt ? n_vt : sp));
+  L.nblk = (int)ceil_div(N, 256);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += region(bytes);
+    return o;
+  };
+  L.lcnt = take((size_t)L.nblk * 4);
+  L.lbad = take((size_t)L.nblk * 4);
+  L.nv = take(4);
+  // part[split][row] of one chunk: splits x token tiles <= kPersistentWGs, so at most
+  // kPersistentWGs x 256 partials for any chunk (a short last chunk has more splits).
+  L.part = take((size_t)kPersistentWGs * kTile * sizeof(float2));
+  L.zlab = take((size_t)L.tc * 4);
+  L.bloss = take((size_t)L.nblk * 8);
+  L.bcnt = take((size_t)L.nblk * 4);
+  L.bbad = take((size_t)L.nblk * 4);
+  L.e2 = take((size_t)L.tc * 4);
+  L.coef = take((size_t)L.tc * 4);
+  L.lab = take((size_t)L.tc * 4);
+  L.oscale = take(4);
+  L.mkeep = take((size_t)L.tc * (size_t)L.ld_m * 4);
+  L.keep = take((size_t)L.tc * (size_t)L.ld * elem_size(dtype));
+  L.total = off;
+  return L;
+}
+
+// Forward and backward without recomputing logits: per token chunk, the logit GEMM keeps
+// the exponentials (fwd_tiles<KEEP>), the chunk's lse and loss terms are combined, the kept
+// values become the dz slab in place (keep_to_dz), and dH (K = the whole vocabulary, so no
+// read-modify-write) and dW (accumulated over chunks in order) are contracted from it:
+// 6 N V D instead of 8 N V D flops.
+template <typename T>
+flce_status single_pass_impl(const T* H, const T* W, const int64_t* y, const float* grad, int N, int D, int V,
+                             int dtype, int64_t ignore_index, float* loss, float* lse, int32_t* n_valid,
+                             int32_t* dev_status, T* dH, float* dW, char* ws, const SpLayout& L, hipStream_t s) {
+  int* lcnt = reinterpret_cast<int*>(ws + L.lcnt);
+  int* lbad = reinterpret_cast<int*>(ws + L.lbad);
+  int32_t* nv = reinterpret_cast<int32_t*>(ws + L.nv);
+  float2* part = reinterpret_cast<float2*>(ws + L.part);
+  float* zlab = reinterpret_cast<float*>(ws + L.zlab);
+  double* bloss = reinterpret_cast<double*>(ws + L.bloss);
+  int* bcnt = reinterpret_cast<int*>(ws + L.bcnt);
+  int* bbad = reinterpret_cast<int*>(ws + L.bbad);
+  float* e2 = reinterpret_cast<float*>(ws + L.e2);
+  float* coef = reinterpret_cast<float*>(ws + L.coef);
+  int* lab = reinterpret_cast<int*>(ws + L.lab);
+  float* oscale = dtype == FLCE_F16 ? reinterpret_cast<float*>(ws + L.oscale) : nullptr;
+  float* mkeep = reinterpret_cast<float*>(ws + L.mkeep);
+  T* keep = reinterpret_cast<T*>(ws + L.keep);
+  const float fixed_scale = dtype == FLCE_F16 ? 16384.f : 0.f;
+  const int ld = (int)L.ld, ld_m = (int)L.ld_m, n_td = (int)ceil_div(D, kTile);
+  const int n_chunks = (int)ceil_div(N, L.tc);
+  auto grid = [](int64_t tiles) { return (unsigned)(tiles < kPersistentWGs ? tiles : kPersistentWGs); };
+  (void)hipGetLastError();
+  label_blocks<<<dim3((unsigned)L.nblk), dim3(256), 0, s>>>(y, N, V, ignore_index, lcnt, lbad);
+  label_total<<<dim3(1), dim3(256), 0, s>>>(lcnt, L.nblk, nv);
+  for (int ci = 0; ci < n_chunks; ++ci) {
+    const int t0 = (int)(ci * L.tc);
+    const int rows = (int)(N - t0 < L.tc ? N - t0 : L.tc);
+    const int ntn = (int)ceil_div(rows, kTile);
+    const int splits = (int)(kPersistentWGs / ntn < 1 ? 1 : (kPersistentWGs / ntn > L.ld / kTile ? L.ld / kTile
+                                                                                                 : kPersistentWGs / ntn));
+    fwd_tiles<T, true><<<dim3((unsigned)(ntn * splits)), dim3(kThreads), 0, s>>>(
+        H + (int64_t)t0 * D, W, y + t0, rows, D, V, ntn, splits, part, zlab, keep, ld, mkeep, ld_m);
+    const int blk0 = t0 / 256;
+    fwd_combine<<<dim3((unsigned)ceil_div(rows, 256)), dim3(256), 0, s>>>(part, splits, zlab, y + t0, rows, V,
+                                                                          ignore_index, lse + t0, bloss + blk0,
+                                                                          bcnt + blk0, bbad + blk0);
+    bwd_prep<<<dim3((unsigned)ceil_div(rows, 256)), dim3(256), 0, s>>>(lse + t0, y + t0, nv, grad, rows, V,
+                                                                       ignore_index, fixed_scale, e2, coef, lab, oscale);
+    const int P = (int)ceil_div(ld / Pack16<T>::K, kDzThreads);
+    const int64_t pieces = (int64_t)rows * P;
+    keep_to_dz<T><<<dim3((unsigned)(pieces < (1 << 20) ? pieces : (1 << 20))), dim3(kDzThreads), 0, s>>>(
+        keep, ld, rows, mkeep, ld_m, e2, coef, lab, pieces, P);
+    const int n_tt = ntn, n_vt = (int)ceil_div(V, kTile);
+    if (dtype == FLCE_F32)
+      bwd_dh<T, false, false><<<dim3(grid((int64_t)n_tt * n_td)), dim3(kThreads), 0, s>>>(
+          keep, ld, W, D, 0, V, t0, rows, n_td, reinterpret_cast<float*>(dH) + (int64_t)t0 * D, dH, oscale);
+    else
+      bwd_dh<T, false, true><<<dim3(grid((int64_t)n_tt * n_td)), dim3(kThreads), 0, s>>>(
+          keep, ld, W, D, 0, V, t0, rows, n_td, reinterpret_cast<float*>(ws), dH, oscale);
+    if (ci > 0)
+      bwd_dw<T, true><<<dim3(grid((int64_t)n_vt * n_td)), dim3(kThreads), 0, s>>>(keep, ld, H, D, t0, rows, 0, V,
+                                                                                  n_td, dW, oscale);
+    else
+      bwd_dw<T, false><<<dim3(grid((int64_t)n_vt * n_td)), dim3(kThreads), 0, s>>>(keep, ld, H, D, t0, rows, 0, V,
+                                                                                   n_td, dW, oscale);
+  }
+  fwd_finalize<<<dim3(1), dim3(256), 0, s>>>(bloss, bcnt, bbad, L.nblk, loss, n_valid, dev_status);
   return launched();
 }
 
@@ -1273,6 +1584,52 @@ flce_status flce_backward(const void* H, const void* W, const int64_t* y, const 
   return backward_impl<float>(reinterpret_cast<const float*>(H), reinterpret_cast<const float*>(W), y, lse, n_valid,
                               grad_loss, (int)N, (int)D, (int)V, dtype, ignore_index, reinterpret_cast<float*>(dH),
                               dW, ws, L, s);
+}
+
+size_t flce_forward_backward_workspace_bytes(int64_t N, int64_t D, int64_t V, int dtype) {
+  if (!sizes_ok(N, D, V, dtype)) return 0;
+  return sp_layout(N, V, dtype).total;
+}
+
+flce_status flce_forward_backward(const void* H, const void* W, const int64_t* y, int64_t N, int64_t D, int64_t V,
+                                  int dtype, int64_t ignore_index, const float* grad_loss, float* loss, float* lse,
+                                  int32_t* n_valid, int32_t* dev_status, void* dH, float* dW, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (!sizes_ok(N, D, V, dtype) || !H || !W || !y || !loss || !lse || !n_valid || !dev_status || !dH || !dW ||
+      !workspace)
+    return FLCE_ERR_INVALID_ARG;
+  const int64_t chunk = dtype == FLCE_F32 ? 4 : 8;
+  if (D % chunk || !aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16) || !aligned(dW, 16) ||
+      !aligned(workspace, 16) || !aligned(y, 8) || !aligned(lse, 4) || !aligned(loss, 4) || !aligned(n_valid, 4) ||
+      !aligned(dev_status, 4) || (grad_loss && !aligned(grad_loss, 4)))
+    return FLCE_ERR_ALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  const SpLayout L = sp_layout(N, V, dtype);
+  if (workspace_bytes >= L.total) {
+    if (dtype == FLCE_BF16)
+      return single_pass_impl<u16>(reinterpret_cast<const u16*>(H), reinterpret_cast<const u16*>(W), y, grad_loss,
+                                   (int)N, (int)D, (int)V, dtype, ignore_index, loss, lse, n_valid, dev_status,
+                                   reinterpret_cast<u16*>(dH), dW, ws, L, s);
+    if (dtype == FLCE_F16)
+      return single_pass_impl<h16>(reinterpret_cast<const h16*>(H), reinterpret_cast<const h16*>(W), y, grad_loss,
+                                   (int)N, (int)D, (int)V, dtype, ignore_index, loss, lse, n_valid, dev_status,
+                                   reinterpret_cast<h16*>(dH), dW, ws, L, s);
+    return single_pass_impl<float>(reinterpret_cast<const float*>(H), reinterpret_cast<const float*>(W), y,
+                                   grad_loss, (int)N, (int)D, (int)V, dtype, ignore_index, loss, lse, n_valid,
+                                   dev_status, reinterpret_cast<float*>(dH), dW, ws, L, s);
+  }
+  // Too small for the single pass: the forward, then the recomputing backward, in the same
+  // workspace (stream order keeps them apart).  Both requirements are checked before either
+  // launches.
+  int64_t tc = 0, vc = 0;
+  if (workspace_bytes < fwd_layout(N, V).total || !pick_chunks(N, D, V, dtype, workspace_bytes, &tc, &vc))
+    return FLCE_ERR_WORKSPACE;
+  const flce_status f = flce_forward(H, W, y, N, D, V, dtype, ignore_index, loss, lse, n_valid, dev_status, workspace,
+                                     workspace_bytes, stream);
+  if (f != FLCE_OK) return f;
+  return flce_backward(H, W, y, lse, n_valid, grad_loss, N, D, V, dtype, ignore_index, dH, dW, workspace,
+                       workspace_bytes, stream);
 }
 
 const char* flce_status_string(int status) {

@@ -213,3 +213,41 @@ def test_norm_argument_errors(B):
     assert _n_bwd(B, dt=0, D=6) == B.FLCE_ERR_ALIGN           # 24-byte fp32 rows
     assert _n_bwd(B, wsb=100) == B.FLCE_ERR_WORKSPACE
 
+
+
+# --- forward and backward in one call ------------------------------------------------
+
+
+def test_single_pass_workspace_formula(B):
+    for N, D, V, dt, es in [(16384, 4096, 128256, 1, 2), (300, 512, 1031, 0, 4), (4097, 256, 32003, 2, 2)]:
+        T = min(-(-N // 256) * 256, 4096)
+        ld = -(-V // 256) * 256
+        nblk = -(-N // 256)
+        expect = (2 * _r(nblk * 4) + _r(4) + _r(256 * 256 * 8) + _r(T * 4) + _r(nblk * 8) + 2 * _r(nblk * 4)
+                  + 3 * _r(T * 4) + _r(4) + _r(T * (ld // 128) * 4) + _r(T * ld * es))
+        assert B.flce_forward_backward_workspace_bytes(N, D, V, dt) == expect
+    # 25% of the 16-bit logit bytes at the Llama-3 shape: the price of skipping the recompute
+    frac = B.flce_forward_backward_workspace_bytes(16384, 4096, 128256, 1) / (16384 * 128256 * 2)
+    assert 0.25 < frac < 0.26
+    assert B.flce_forward_backward_workspace_bytes(0, 64, 64, 1) == 0
+
+
+# Every call below has an argument the library rejects before launching anything.
+def _fb(B, H=A16, W=A16, y=A16, N=512, D=64, V=1024, dt=1, g=None, loss=A16, lse=A16, nv=A16, st=A16, dH=A16,
+        dW=A16, ws=A16, wsb=10**5):
+    return B.lib.flce_forward_backward(H, W, y, N, D, V, dt, -100, g, loss, lse, nv, st, dH, dW, ws, wsb, None)
+
+
+def test_forward_backward_argument_errors(B):
+    assert _fb(B, H=None) == B.FLCE_ERR_INVALID_ARG
+    assert _fb(B, dW=None) == B.FLCE_ERR_INVALID_ARG
+    assert _fb(B, N=0) == B.FLCE_ERR_INVALID_ARG
+    assert _fb(B, dt=7) == B.FLCE_ERR_INVALID_ARG
+    assert _fb(B, D=12) == B.FLCE_ERR_ALIGN
+    assert _fb(B, dH=A16 + 8) == B.FLCE_ERR_ALIGN
+    assert _fb(B, g=A16 + 2) == B.FLCE_ERR_ALIGN
+    # enough for neither schedule (the forward alone would fit 10**5 bytes only at tiny N)
+    assert _fb(B, wsb=1000) == B.FLCE_ERR_WORKSPACE
+    # enough for the forward but not the backward: rejected before the forward launches
+    fwd_only = B.flce_workspace_bytes(512, 64, 1024, 1) // 16
+    assert _fb(B, wsb=fwd_only) == B.FLCE_ERR_WORKSPACE

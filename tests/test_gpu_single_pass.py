@@ -1,0 +1,165 @@
+"""GPU parity of flce_forward_backward (include/flce.h), the forward and backward in one
+call, against the fp64 oracle: the single-pass schedule (workspace of
+flce_forward_backward_workspace_bytes) on small ragged cases, several token chunks with a
+short last one, every dtype, an upstream gradient and a custom ignore_index, and the
+Llama-3-shaped full size; and the fallback schedule (a smaller workspace), which must
+equal separate flce_forward + flce_backward calls bit for bit.
+
+Tolerances are the fused path's (tests/flce_run.py): the single pass rounds p~ = exp(z - m)
+to the input type and then rounds dz once more, one extra rounding of the same size as
+the slab's own.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_cross_entropy_lm_amd import inputs as I
+from flce_run import TOL, compare, rel_fro, run_gpu
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from linear_cross_entropy_lm_amd import binding  # noqa: F401  (fails loudly if not built)
+
+
+def run_fb(inp, g=None, ignore_index=-100, single=True, device="cuda:0") -> dict:
+    from linear_cross_entropy_lm_amd import binding as B
+    H, W, y = inp.device_tensors(device)
+    N, D = H.shape
+    V = W.shape[0]
+    sp_bytes = B.flce_forward_backward_workspace_bytes(N, D, V, H.dtype)
+    two_bytes = B.flce_workspace_bytes(N, D, V, H.dtype)
+    if not single:
+        # the fallback needs a workspace that fits the two calls but not the single pass
+        assert two_bytes < sp_bytes, (two_bytes, sp_bytes)
+    ws = torch.empty(sp_bytes if single else two_bytes, dtype=torch.uint8, device=device)
+    loss = torch.empty(1, dtype=torch.float32, device=device)
+    lse = torch.empty(N, dtype=torch.float32, device=device)
+    nv = torch.empty(1, dtype=torch.int32, device=device)
+    st = torch.full((1,), -7, dtype=torch.int32, device=device)
+    dH = torch.full_like(H, float("nan"))
+    dW = torch.full((V, D), float("nan"), dtype=torch.float32, device=device)
+    gl = None if g is None else torch.tensor([g], dtype=torch.float32, device=device)
+    B.flce_forward_backward(H, W, y, gl, loss, lse, nv, st, dH, dW, ws, ignore_index)
+    torch.cuda.synchronize()
+    return dict(loss=float(loss.item()), lse=lse.cpu().double().numpy(), n_valid=int(nv.item()),
+                status=int(st.item()), dH=dH.float().cpu().double().numpy(), dW=dW.cpu().double().numpy())
+
+
+CASES = [
+    ("tiny_f32", None),
+    ("ragged_bf16", I.case(300, 512, 1031, "bf16", seed=71)),
+    ("ragged_f32", I.case(300, 512, 1031, "f32", seed=72)),
+    ("ragged_f16", I.case(300, 512, 1031, "f16", seed=73)),
+    ("raggedD_bf16", I.case(513, 264, 2500, "bf16", seed=74, ignore_frac=0.2)),
+    ("zipf_bf16", I.case(640, 256, 4099, "bf16", seed=75, label_dist="zipf")),
+    # two token chunks (4096 + 404 rows: the short one runs with more vocabulary splits)
+    ("two_chunks_bf16", I.case(4500, 256, 3000, "bf16", seed=76)),
+    ("two_chunks_f16", I.case(4500, 256, 3000, "f16", seed=77)),
+    ("V1_f32", I.case(65, 128, 1, "f32", seed=78, ignore_frac=0.0)),
+]
+
+
+@pytest.mark.parametrize("name,cfg", CASES, ids=[c[0] for c in CASES])
+def test_single_pass_parity(name, cfg):
+    cfg = cfg or I.CONFIGS[name]
+    print("case", cfg.describe(), flush=True)
+    inp = I.generate(cfg)
+    # fp16 runs with a loss scale, as fp16 training does: at g = 1 and N_valid in the
+    # thousands, dH entries fall below fp16's smallest normal
+    g = 1024.0 if cfg.dtype == "f16" else None
+    got = run_fb(inp, g=g)
+    ref = oracle.forward_backward(inp.h64(), inp.w64(), inp.y64(), g=g or 1.0)
+    err = compare(got, ref, cfg.dtype)
+    assert got["status"] == 0
+    print("errors", err, flush=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_single_pass_grad_and_ignore_index(dtype):
+    cfg = I.case(400, 256, 900, dtype, seed=79, ignore_frac=0.0)
+    inp = I.generate(cfg)
+    y = inp.y.clone()
+    y[::6] = 11
+    inp = I.Inputs(cfg, inp.H, inp.W, y)
+    got = run_fb(inp, g=-2.5, ignore_index=11)
+    ref = oracle.forward_backward(inp.h64(), inp.w64(), inp.y64(), ignore_index=11, g=-2.5)
+    compare(got, ref, dtype)
+
+
+def test_single_pass_all_rows_ignored():
+    cfg = I.case(300, 256, 1000, "bf16", seed=80)
+    inp = I.generate(cfg)
+    inp = I.Inputs(cfg, inp.H, inp.W, torch.full((300,), -100, dtype=torch.int64))
+    got = run_fb(inp)
+    assert got["n_valid"] == 0 and got["loss"] == 0.0
+    assert np.all(got["dH"] == 0.0) and np.all(got["dW"] == 0.0)
+
+
+def test_single_pass_bitwise_deterministic():
+    inp = I.generate(I.case(4500, 256, 3000, "bf16", seed=81))
+    a, b = run_fb(inp), run_fb(inp)
+    for k in ("loss", "lse", "dH", "dW"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_fallback_equals_forward_then_backward(dtype):
+    """A workspace too small for the single pass runs the two-call schedule: identical bits.
+    (V > 8192, so the two-call workspace, with its 8192-wide vocabulary chunks, is the
+    smaller one.)"""
+    inp = I.generate(I.case(700, 256, 20000, dtype, seed=82))
+    a = run_fb(inp, g=0.75, single=False)
+    b = run_gpu(inp, g=0.75)
+    for k in ("loss", "lse", "dH", "dW"):
+        assert np.array_equal(np.asarray(a[k]), np.asarray(b[k])), k
+
+
+def test_single_pass_fullsize_llama3():
+    """16384 x 4096 x 128256 bf16 in one call (four token chunks of 4096): loss, every
+    row's lse, dH and dW on the sampled rows against the stored oracle run, and the
+    properties that hold at any size on the whole output."""
+    from linear_cross_entropy_lm_amd import binding as B
+    cfg = I.CONFIGS["llama3"]
+    print("case", cfg.describe(), flush=True)
+    gold = np.load(os.path.join(GOLDEN, "fullsize_llama3.npz"))
+    inp = I.generate(cfg)
+    assert inp.digest() == str(gold["digest"]), "seeded inputs differ from the stored oracle run"
+    dev = "cuda:0"
+    H, W, y = inp.device_tensors(dev)
+    N, D, V = cfg.N, cfg.D, cfg.V
+    ws = torch.empty(B.flce_forward_backward_workspace_bytes(N, D, V, H.dtype), dtype=torch.uint8, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    nv = torch.empty(1, dtype=torch.int32, device=dev)
+    st = torch.empty(1, dtype=torch.int32, device=dev)
+    dH = torch.full_like(H, float("nan"))
+    dW = torch.full((V, D), float("nan"), dtype=torch.float32, device=dev)
+    B.flce_forward_backward(H, W, y, None, loss, lse, nv, st, dH, dW, ws)
+    torch.cuda.synchronize()
+    tol = TOL["bf16"]
+    assert int(st.item()) == 0 and int(nv.item()) == int(gold["n_valid"])
+    e_loss = abs(loss.item() - float(gold["loss"])) / float(gold["loss"])
+    e_lse = float(np.max(np.abs(lse.cpu().double().numpy() - gold["lse"]) / np.abs(gold["lse"])))
+    rows = torch.from_numpy(gold["dh_rows"]).to(dev)
+    vrows = torch.from_numpy(gold["dw_rows"]).to(dev)
+    e_dh = rel_fro(dH[rows].float().cpu().numpy(), gold["dh"])
+    e_dw = rel_fro(dW[vrows].cpu().numpy(), gold["dw"])
+    print(f"loss {loss.item():.6f} (oracle {float(gold['loss']):.6f}) rel {e_loss:.2e}; lse {e_lse:.2e}; "
+          f"dH rows {e_dh:.2e}; dW rows {e_dw:.2e}", flush=True)
+    assert e_loss <= tol["loss"] and e_lse <= tol["lse"] and e_dh <= tol["grad"] and e_dw <= tol["grad"]
+    assert bool(torch.isfinite(dW).all()) and bool(torch.isfinite(dH.float()).all())
+    assert bool((dH[y == -100] == 0).all())
+    colsum = dW.double().sum(dim=0).norm().item()
+    assert colsum <= 1e-2 * dW.double().norm().item()
+    lhs = (dW.double() * W.double()).sum().item()
+    rhs = (dH.double() * H.double()).sum().item()
+    assert abs(lhs - rhs) <= 1e-2 * abs(lhs)
