@@ -284,7 +284,7 @@ def run_single(args) -> dict:
     dev = "cuda:0"
     H, W, y = inp.device_tensors(dev)
     N, D, V = cfg.N, cfg.D, cfg.V
-    ws_bytes = B.flce_forward_backward_workspace_bytes(N, D, V, H.dtype)
+    ws_bytes = int(B.flce_forward_backward_workspace_bytes(N, D, V, H.dtype) * args.sp_workspace)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     loss = torch.empty(1, dtype=torch.float32, device=dev)
     lse = torch.empty(N, dtype=torch.float32, device=dev)
@@ -502,6 +502,9 @@ def main() -> int:
                          "call without logit recompute (25%% scratch); ce: cross-entropy over materialised "
                          "logits; norm: the RMSNorm that produces H")
     ap.add_argument("--workload", default=None, help="default llama3 (fused), ce_llama3 (ce), norm_llama3 (norm)")
+    ap.add_argument("--sp-workspace", type=float, default=1.0, metavar="F",
+                    help="--path single: workspace = F x the least single-pass workspace (2.0: token "
+                         "chunks of 8192 at the Llama-3 shape)")
     ap.add_argument("--cpu-rows", type=int, default=None,
                     help="rows of the oracle sample (default 1024 fused, 8192 ce: 10-20 s of CPU work)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -135,12 +135,14 @@ flce_status flce_backward(const void* H, const void* W, const int64_t* y, const 
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Single-pass workspace: the bytes flce_forward_backward needs to run without recomputing
- * the logits.  Token chunks of T = min(N, 4096) rows (rounded up to 256) keep, for the
- * whole vocabulary, p~ = exp(z - m) in the input type (T x V' elements, V' = V rounded up
- * to 256) and the maxima m of each 128-row half tile in fp32 (T x V'/128), plus a few MB
- * of per-row and per-block terms: about T V' es + 4 T V'/128 bytes (1.07 GB, 25% of the
- * 16-bit N x V logit bytes, at N = 16384, V = 128256, bf16).  0 for invalid sizes.
+ * Single-pass workspace: the least bytes flce_forward_backward needs to run without
+ * recomputing the logits.  Token chunks of T = min(N, 4096) rows (rounded up to 256) keep,
+ * for the whole vocabulary, p~ = exp(z - m) in the input type (T x V' elements, V' = V
+ * rounded up to 256) and the maxima m of each 128-row half tile in fp32 (T x V'/128), plus
+ * a few MB of per-row and per-block terms: about T V' es + 4 T V'/128 bytes (1.07 GB, 25%
+ * of the 16-bit N x V logit bytes, at N = 16384, V = 128256, bf16).  A larger workspace
+ * lets the call take larger chunks (multiples of 4096 rows, up to N): fewer passes of
+ * dW's read-modify-write.  0 for invalid sizes.
  */
 size_t flce_forward_backward_workspace_bytes(int64_t N, int64_t D, int64_t V, int dtype);
 

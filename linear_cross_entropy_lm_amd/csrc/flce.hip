@@ -1404,9 +1404,9 @@ flce_status backward_impl(const T* H, const T* W, const int64_t* y, const float*
   return launched();
 }
 
-// Single-pass workspace: token chunks of tc rows (min(N, 4096) rounded up to 256) keep
-// their exponentials for the whole vocabulary: keep [tc][ld] in the input type, ld = V
-// rounded up to 256, and mkeep [tc][ld / 128] fp32; plus the forward partials of one chunk,
+// Single-pass workspace for token chunks of tc rows (a multiple of 256): each chunk keeps
+// its exponentials for the whole vocabulary, keep [tc][ld] in the input type (ld = V
+// rounded up to 256) and mkeep [tc][ld / 128] fp32; plus the forward partials of one chunk,
 // per-row terms of one chunk, and block sums over all N rows.
 struct SpLayout {
   int64_t tc, ld, ld_m;
@@ -1414,9 +1414,9 @@ struct SpLayout {
   size_t lcnt, lbad, nv, part, zlab, bloss, bcnt, bbad, e2, coef, lab, oscale, mkeep, keep, total;
 };
 
-SpLayout sp_layout(int64_t N, int64_t V, int dtype) {
+SpLayout sp_layout(int64_t N, int64_t V, int dtype, int64_t tc) {
   SpLayout L;
-  L.tc = round_up(N < kDefaultTokenChunk ? N : kDefaultTokenChunk, kTile);
+  L.tc = tc;
   L.ld = round_up(V, kTile);
   L.ld_m = L.ld / 128;
   const int64_t ntn = L.tc / kTile, n_vt = L.ld / kTile;
@@ -1447,6 +1447,24 @@ SpLayout sp_layout(int64_t N, int64_t V, int dtype) {
   L.keep = take((size_t)L.tc * (size_t)L.ld * elem_size(dtype));
   L.total = off;
   return L;
+}
+
+// The smallest single-pass chunk: min(N, 4096) rows rounded up to 256.
+int64_t sp_min_chunk(int64_t N) { return round_up(N < kDefaultTokenChunk ? N : kDefaultTokenChunk, kTile); }
+
+// The largest chunk whose single-pass layout fits `ws`: the smallest chunk, then multiples
+// of 4096 rows up to N (a chunk of all N rows needs no read-modify-write of dW).  False if
+// even the smallest does not fit.
+bool sp_pick(int64_t N, int64_t V, int dtype, size_t ws, SpLayout* out) {
+  int64_t best = sp_min_chunk(N);
+  if (sp_layout(N, V, dtype, best).total > ws) return false;
+  for (int64_t tc = 2 * kDefaultTokenChunk; tc - kDefaultTokenChunk < N; tc += kDefaultTokenChunk) {
+    const int64_t t = round_up(tc < N ? tc : N, kTile);
+    if (sp_layout(N, V, dtype, t).total > ws) break;
+    best = t;
+  }
+  *out = sp_layout(N, V, dtype, best);
+  return true;
 }
 
 // Forward and backward without recomputing logits: per token chunk, the logit GEMM keeps
@@ -1588,7 +1606,7 @@ flce_status flce_backward(const void* H, const void* W, const int64_t* y, const 
 
 size_t flce_forward_backward_workspace_bytes(int64_t N, int64_t D, int64_t V, int dtype) {
   if (!sizes_ok(N, D, V, dtype)) return 0;
-  return sp_layout(N, V, dtype).total;
+  return sp_layout(N, V, dtype, sp_min_chunk(N)).total;
 }
 
 flce_status flce_forward_backward(const void* H, const void* W, const int64_t* y, int64_t N, int64_t D, int64_t V,
@@ -1605,8 +1623,8 @@ flce_status flce_forward_backward(const void* H, const void* W, const int64_t* y
     return FLCE_ERR_ALIGN;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = reinterpret_cast<char*>(workspace);
-  const SpLayout L = sp_layout(N, V, dtype);
-  if (workspace_bytes >= L.total) {
+  SpLayout L;
+  if (sp_pick(N, V, dtype, workspace_bytes, &L)) {
     if (dtype == FLCE_BF16)
       return single_pass_impl<u16>(reinterpret_cast<const u16*>(H), reinterpret_cast<const u16*>(W), y, grad_loss,
                                    (int)N, (int)D, (int)V, dtype, ignore_index, loss, lse, n_valid, dev_status,

@@ -30,7 +30,7 @@ def _gpu():
     from linear_cross_entropy_lm_amd import binding  # noqa: F401  (fails loudly if not built)
 
 
-def run_fb(inp, g=None, ignore_index=-100, single=True, device="cuda:0") -> dict:
+def run_fb(inp, g=None, ignore_index=-100, single=True, ws_factor=1.0, device="cuda:0") -> dict:
     from linear_cross_entropy_lm_amd import binding as B
     H, W, y = inp.device_tensors(device)
     N, D = H.shape
@@ -40,7 +40,7 @@ def run_fb(inp, g=None, ignore_index=-100, single=True, device="cuda:0") -> dict
     if not single:
         # the fallback needs a workspace that fits the two calls but not the single pass
         assert two_bytes < sp_bytes, (two_bytes, sp_bytes)
-    ws = torch.empty(sp_bytes if single else two_bytes, dtype=torch.uint8, device=device)
+    ws = torch.empty(int(sp_bytes * ws_factor) if single else two_bytes, dtype=torch.uint8, device=device)
     loss = torch.empty(1, dtype=torch.float32, device=device)
     lse = torch.empty(N, dtype=torch.float32, device=device)
     nv = torch.empty(1, dtype=torch.int32, device=device)
@@ -83,6 +83,18 @@ def test_single_pass_parity(name, cfg):
     print("errors", err, flush=True)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_single_pass_one_chunk(dtype):
+    """A workspace 1.2x the least: the 4500 rows fit one chunk of 4608 (dW written once,
+    never read back)."""
+    cfg = I.case(4500, 256, 3000, dtype, seed=83)
+    inp = I.generate(cfg)
+    g = 1024.0 if dtype == "f16" else None
+    got = run_fb(inp, g=g, ws_factor=1.2)
+    ref = oracle.forward_backward(inp.h64(), inp.w64(), inp.y64(), g=g or 1.0)
+    compare(got, ref, dtype)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_single_pass_grad_and_ignore_index(dtype):
     cfg = I.case(400, 256, 900, dtype, seed=79, ignore_frac=0.0)
@@ -123,10 +135,11 @@ def test_fallback_equals_forward_then_backward(dtype):
         assert np.array_equal(np.asarray(a[k]), np.asarray(b[k])), k
 
 
-def test_single_pass_fullsize_llama3():
-    """16384 x 4096 x 128256 bf16 in one call (four token chunks of 4096): loss, every
-    row's lse, dH and dW on the sampled rows against the stored oracle run, and the
-    properties that hold at any size on the whole output."""
+@pytest.mark.parametrize("ws_factor", [1.0, 2.0])
+def test_single_pass_fullsize_llama3(ws_factor):
+    """16384 x 4096 x 128256 bf16 in one call (four token chunks of 4096, or two of 8192
+    with twice the workspace): loss, every row's lse, dH and dW on the sampled rows against
+    the stored oracle run, and the properties that hold at any size on the whole output."""
     from linear_cross_entropy_lm_amd import binding as B
     cfg = I.CONFIGS["llama3"]
     print("case", cfg.describe(), flush=True)
@@ -136,7 +149,8 @@ def test_single_pass_fullsize_llama3():
     dev = "cuda:0"
     H, W, y = inp.device_tensors(dev)
     N, D, V = cfg.N, cfg.D, cfg.V
-    ws = torch.empty(B.flce_forward_backward_workspace_bytes(N, D, V, H.dtype), dtype=torch.uint8, device=dev)
+    ws = torch.empty(int(B.flce_forward_backward_workspace_bytes(N, D, V, H.dtype) * ws_factor), dtype=torch.uint8,
+                     device=dev)
     loss = torch.empty(1, dtype=torch.float32, device=dev)
     lse = torch.empty(N, dtype=torch.float32, device=dev)
     nv = torch.empty(1, dtype=torch.int32, device=dev)
