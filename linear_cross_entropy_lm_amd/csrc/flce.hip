@@ -582,7 +582,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles(const T* __restrict__ H
   const int n_vt = (V + kTile - 1) / kTile;
   const int count = (n_vt - sp + splits - 1) / splits;
   const int n0 = nt * kTile;
-  constexpr int BK = kStageK<T>;
   const int ldb = D * (int)sizeof(T);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, t = threadIdx.x;
   const int wm = wave / kWavesN, wn = wave % kWavesN, lr = lane & 31, lh = lane >> 5;
@@ -874,7 +873,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dz(const T* __restrict__ H, c
                                                        const int* __restrict__ lab, T* __restrict__ slab,
                                                        int ld_slab) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
-  constexpr int BK = kStageK<T>;
   const int ldb = D * (int)sizeof(T);
   const int tiles = ((vc_act + kTile - 1) / kTile) * n_tiles_t;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1053,7 +1051,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dw(const T* __restrict__ slab
                                                        const float* __restrict__ oscale) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   const float sc = oscale ? *oscale : 1.f;
-  constexpr int BK = kStageK<T>;
   const int es = (int)sizeof(T);
   const int tiles = ((vc_act + kTile - 1) / kTile) * n_tiles_d;
   const int n_vt = (vc_act + kTile - 1) / kTile;
