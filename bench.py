@@ -492,6 +492,55 @@ def _time_steps(args, step, stream):
     return ms, fwd_ms, step_ms, peak_delta
 
 
+OCCUPANCY_COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT",
+                      "SQ_LDS_ADDR_CONFLICT", "SQ_BUSY_CU_CYCLES", "SQ_WAIT_INST_LDS", "SQ_LDS_DATA_FIFO_FULL")
+MI355X_XCDS, MI355X_CUS, MI355X_SIMDS = 8, 256, 1024
+
+
+def summarize_occupancy(csv_dir: str, min_us: float = 100.0) -> list[dict]:
+    """Per kernel (name and launch shape), from one rocprofv3 --pmc run of OCCUPANCY_COUNTERS
+    (--output-format csv, whose rows carry each dispatch's start and end): the mean duration,
+    the shader clock (GRBM_GUI_ACTIVE is summed over the 8 XCDs, so one XCD's busy cycles
+    over the duration), the fraction of those cycles the MFMA pipes are busy (per SIMD), the
+    product clock x MFMA busy (GHz of fully busy MFMA issue), and the LDS-active, LDS
+    bank-conflict and LDS-issue-wait fractions (per CU, per CU, per SIMD; the wait counter is
+    in units of 4 cycles).  Kernels whose mean duration is under min_us are left out."""
+    import csv
+    import glob
+    import re
+    disp = {}
+    for path in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                key = (path, r["Dispatch_Id"])
+                d = disp.setdefault(key, {"name": r["Kernel_Name"], "grid": int(r["Grid_Size"]),
+                                          "wg": int(r["Workgroup_Size"]),
+                                          "s": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    agg = {}
+    for d in disp.values():
+        if not all(c in d for c in OCCUPANCY_COUNTERS):
+            continue
+        name = re.sub(r"\(anonymous namespace\)::|void ", "", d["name"]).split("(")[0].strip()
+        a = agg.setdefault((name, d["grid"] // d["wg"], d["wg"]), {c: 0.0 for c in OCCUPANCY_COUNTERS + ("s", "n")})
+        a["n"] += 1
+        for c in OCCUPANCY_COUNTERS + ("s",):
+            a[c] += d[c]
+    out = []
+    for (name, grid, wg), a in agg.items():
+        if a["s"] / a["n"] * 1e6 < min_us:
+            continue
+        cyc = a["GRBM_GUI_ACTIVE"] / MI355X_XCDS
+        clk = cyc / a["s"] / 1e9
+        mfma = a["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * MI355X_SIMDS)
+        out.append({"kernel": name, "grid": grid, "workgroup": wg, "dispatches": int(a["n"]),
+                    "mean_us": a["s"] / a["n"] * 1e6, "clock_ghz": clk, "mfma_busy": mfma,
+                    "mfma_busy_ghz": clk * mfma, "lds_active": a["SQ_LDS_IDX_ACTIVE"] / (cyc * MI355X_CUS),
+                    "lds_bank_conflict": a["SQ_LDS_BANK_CONFLICT"] / (cyc * MI355X_CUS),
+                    "lds_issue_wait": 4 * a["SQ_WAIT_INST_LDS"] / (cyc * MI355X_SIMDS)})
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
@@ -513,8 +562,15 @@ def main() -> int:
     ap.add_argument("--summarize-counters", metavar="DIR",
                     help="only write the path's traffic record from rocprofv3 counter runs under DIR "
                          "(subdirectories F, W, FC, WC); no GPU needed")
+    ap.add_argument("--summarize-occupancy", metavar="DIR",
+                    help="only print, per kernel, clock, MFMA-busy and LDS figures from one rocprofv3 --pmc "
+                         "run of bench.OCCUPANCY_COUNTERS under DIR; no GPU needed")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     args = ap.parse_args()
+    if args.summarize_occupancy:
+        for rec in summarize_occupancy(args.summarize_occupancy):
+            print(json.dumps(rec), flush=True)
+        return 0
     if args.summarize_counters:
         print(json.dumps(summarize_counters(args.summarize_counters, args.copy_bytes, args.path)), flush=True)
         return 0

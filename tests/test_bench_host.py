@@ -78,3 +78,31 @@ def test_code_digest_ignores_comments_only():
     other = "int f(int x) { return 3 * x; }\n"
     assert bench.code_digest(src) == bench.code_digest(same)
     assert bench.code_digest(src) != bench.code_digest(other)
+
+
+def test_summarize_occupancy(tmp_path):
+    """Two dispatches of one kernel lasting 1 ms each at 2.0 GHz: GRBM_GUI_ACTIVE is summed
+    over the 8 XCDs (8 x 2e6 cycles); MFMA busy half of every SIMD's cycles; LDS active a
+    quarter of every CU's; a kernel shorter than 100 us is left out."""
+    cyc = 2e6
+    vals = {"GRBM_GUI_ACTIVE": 8 * cyc, "SQ_VALU_MFMA_BUSY_CYCLES": 0.5 * cyc * 1024,
+            "SQ_LDS_IDX_ACTIVE": 0.25 * cyc * 256, "SQ_LDS_BANK_CONFLICT": 0.01 * cyc * 256,
+            "SQ_LDS_ADDR_CONFLICT": 0.0, "SQ_BUSY_CU_CYCLES": cyc * 256 / 4,
+            "SQ_WAIT_INST_LDS": 0.1 * cyc * 1024 / 4, "SQ_LDS_DATA_FIFO_FULL": 0.0}
+    assert set(vals) == set(bench.OCCUPANCY_COUNTERS)
+    with open(tmp_path / "p_counter_collection.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Grid_Size", "Workgroup_Size", "Counter_Name", "Counter_Value",
+                    "Start_Timestamp", "End_Timestamp"])
+        for d, (name, dur) in enumerate([("void (anonymous namespace)::gemm<bf16>(int)", 1_000_000)] * 2
+                                        + [("void small(int)", 50_000)]):
+            for c, v in vals.items():
+                w.writerow([d, name, 131072, 512, c, v, 1000, 1000 + dur])
+    recs = bench.summarize_occupancy(str(tmp_path))
+    assert len(recs) == 1
+    r = recs[0]
+    assert (r["kernel"], r["grid"], r["workgroup"], r["dispatches"]) == ("gemm<bf16>", 256, 512, 2)
+    assert r["mean_us"] == pytest.approx(1000.0) and r["clock_ghz"] == pytest.approx(2.0)
+    assert r["mfma_busy"] == pytest.approx(0.5) and r["mfma_busy_ghz"] == pytest.approx(1.0)
+    assert r["lds_active"] == pytest.approx(0.25) and r["lds_bank_conflict"] == pytest.approx(0.01)
+    assert r["lds_issue_wait"] == pytest.approx(0.1)
