@@ -151,14 +151,16 @@ __device__ __forceinline__ u32x4 dma_rsrc(const void* base, u32 bytes) {
 // compiler's counts for those stay conservative.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma_operand(const u32x4& r, char* op, const u32 (&v)[kDmaPerWave]) {
+__device__ __forceinline__ void dma_one(const u32x4& r, char* op, u32 v, int i) {
   const u32 w = (u32)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const u32 base = (u32)reinterpret_cast<uintptr_t>((lds_void*)op) + w * (u32)(kDmaPerWave * kDmaBytes);
+  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds" ::"v"(v),
+               "s"(base + (u32)(i * kDmaBytes)), "s"(r)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma_operand(const u32x4& r, char* op, const u32 (&v)[kDmaPerWave]) {
 #pragma unroll
-  for (int i = 0; i < kDmaPerWave; ++i)
-    asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds" ::"v"(v[i]),
-                 "s"(base + (u32)(i * kDmaBytes)), "s"(r)
-                 : "memory", "m0");
+  for (int i = 0; i < kDmaPerWave; ++i) dma_one(r, op, v[i], i);
 }
 #pragma clang diagnostic pop
 
@@ -199,12 +201,16 @@ template <typename T> struct KTile {
       voff[i] = (u32)r * (u32)ld_bytes + (u32)c * 16u;
     }
   }
+  __device__ __forceinline__ u32 off(int i, int k0) const {
+    return k0 + kc[i] < k_lim ? voff[i] + (u32)k0 * (u32)sizeof(T) : kOOB;
+  }
   __device__ __forceinline__ void load(char* op, int k0) const {
     u32 v[kDmaPerWave];
 #pragma unroll
-    for (int i = 0; i < kDmaPerWave; ++i) v[i] = k0 + kc[i] < k_lim ? voff[i] + (u32)k0 * (u32)sizeof(T) : kOOB;
+    for (int i = 0; i < kDmaPerWave; ++i) v[i] = off(i, k0);
     dma_operand(rsrc, op, v);
   }
+  __device__ __forceinline__ void load_one(char* op, int k0, int i) const { dma_one(rsrc, op, off(i, k0), i); }
 };
 
 // Rows MN-contiguous in HBM: element (tile element e, k) at base + k * ld_bytes + e * sizeof(T)
@@ -255,12 +261,14 @@ template <> struct MNTile<u16> {
       voff[i] = c * 8 < cols_ok ? (u32)k * ld + (u32)c * 16u : kOOB;
     }
   }
+  __device__ __forceinline__ u32 off(int i, int k0) const { return voff[i] == kOOB ? kOOB : voff[i] + (u32)k0 * ld; }
   __device__ __forceinline__ void load(char* op, int k0) const {
     u32 v[kDmaPerWave];
 #pragma unroll
-    for (int i = 0; i < kDmaPerWave; ++i) v[i] = voff[i] == kOOB ? kOOB : voff[i] + (u32)k0 * ld;
+    for (int i = 0; i < kDmaPerWave; ++i) v[i] = off(i, k0);
     dma_operand(rsrc, op, v);
   }
+  __device__ __forceinline__ void load_one(char* op, int k0, int i) const { dma_one(rsrc, op, off(i, k0), i); }
 };
 
 // fp16 tiles move and transpose exactly like bf16 ones.
@@ -303,12 +311,14 @@ template <> struct MNTile<float> {
       voff[i] = c * 4 < cols_ok ? (u32)k * ld + (u32)c * 16u : kOOB;
     }
   }
+  __device__ __forceinline__ u32 off(int i, int k0) const { return voff[i] == kOOB ? kOOB : voff[i] + (u32)k0 * ld; }
   __device__ __forceinline__ void load(char* op, int k0) const {
     u32 v[kDmaPerWave];
 #pragma unroll
-    for (int i = 0; i < kDmaPerWave; ++i) v[i] = voff[i] == kOOB ? kOOB : voff[i] + (u32)k0 * ld;
+    for (int i = 0; i < kDmaPerWave; ++i) v[i] = off(i, k0);
     dma_operand(rsrc, op, v);
   }
+  __device__ __forceinline__ void load_one(char* op, int k0, int i) const { dma_one(rsrc, op, off(i, k0), i); }
 };
 
 // ---------------------------------------------------------------------------------
@@ -406,6 +416,62 @@ __device__ __forceinline__ void dma_barrier() {
   __syncthreads();
 }
 
+// Position g of mma_frags' product order: its A block (want_j false) or B block.
+constexpr int mma_block(int g, bool want_j) {
+  int n = 0;
+  for (int r = 0; r < kBM + kBN; ++r)
+    for (int i = 0; i < kBM; ++i)
+      for (int j = 0; j < kBN; ++j)
+        if (max_i(rank_a(i), rank_b(j)) == r) {
+          if (n == g) return want_j ? j : i;
+          ++n;
+        }
+  return 0;
+}
+
+// Step 3 of a slice, after the barrier.  Product g (on fragments already in registers) is
+// followed by its share of the DMA loads of the slice after next into `cur` (A's, then B's)
+// and of the reads of `nxt`'s step-0 fragments, each group pinned in that order, so the
+// loads issue between products instead of in one burst ahead of them.
+template <typename T, typename TA, typename TB, int G>
+__device__ __forceinline__ void step3_slot(f32x16 (&acc)[kBM][kBN], u32x4 (&fa0)[kBM], u32x4 (&fb0)[kBN],
+                                           const u32x4 (&fa1)[kBM], const u32x4 (&fb1)[kBN], char* cur,
+                                           const char* nxt, const TA& A, const TB& B, const FragAddr& aa,
+                                           const FragAddr& ab, int k_load) {
+  constexpr int NG = kBM * kBN, ND = 2 * kDmaPerWave, NR = kBM + kBN;
+  if constexpr (G < NG) {
+    constexpr int i = mma_block(G, false), j = mma_block(G, true);
+    Mfma<T>::run(acc[i][j], fa1[i], fb1[j]);
+#pragma unroll
+    for (int d = G * ND / NG; d < (G + 1) * ND / NG; ++d) {
+      if (d < kDmaPerWave)
+        A.load_one(cur, k_load, d);
+      else
+        B.load_one(cur + kOperandBytes, k_load, d - kDmaPerWave);
+    }
+#pragma unroll
+    for (int r = G * NR / NG; r < (G + 1) * NR / NG; ++r) {
+#pragma unroll
+      for (int ii = 0; ii < kBM; ++ii)
+        if (rank_a(ii) == r) fa0[ii] = TA::frag(nxt, aa, ii, 0);
+#pragma unroll
+      for (int jj = 0; jj < kBN; ++jj)
+        if (rank_b(jj) == r) fb0[jj] = TB::frag(nxt + kOperandBytes, ab, jj, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    step3_slot<T, TA, TB, G + 1>(acc, fa0, fb0, fa1, fb1, cur, nxt, A, B, aa, ab, k_load);
+  }
+}
+
+// Step 3's schedule: with two K-contiguous operands (one 16-byte read per fragment) the
+// products are interleaved with the DMA loads and the next fragments' reads (the forward
+// and the dz tiles measured 1.3-3.3% faster on three machines, or the same); with a
+// transposed operand (two or four reads per fragment) the reads go first, then the loads,
+// then the products, which measured 1-4% faster there than interleaving either way.
+template <typename TA, typename TB> constexpr bool step3_interleaved() {
+  return TA::kFragReads == 1 && TB::kFragReads == 1;
+}
+
 // One K slice (four 16-element K steps) on LDS stage `cur`.  On entry the fragments of
 // step 0 are in fa0/fb0 and the DMA loads of the next slice into `nxt` are in flight.
 // Steps 0-2 read each next step's fragments one step ahead; the barrier then waits for
@@ -433,11 +499,15 @@ __device__ __forceinline__ void gemm_slice(f32x16 (&acc)[kBM][kBN], char* cur, c
   __builtin_amdgcn_s_setprio(0);
   dma_barrier();
   __builtin_amdgcn_s_setprio(1);
-  read_frags<TA, TB>(fa0, fb0, nxt, aa, ab, 0);
-  A.load(cur, k_load);
-  B.load(cur + kOperandBytes, k_load);
-  mma_frags<T>(acc, fa1, fb1);
-  sched_step<M, R, 0, 0>();  // step 3 under the next fragment reads and the loads
+  if constexpr (step3_interleaved<TA, TB>()) {
+    step3_slot<T, TA, TB, 0>(acc, fa0, fb0, fa1, fb1, cur, nxt, A, B, aa, ab, k_load);
+  } else {
+    read_frags<TA, TB>(fa0, fb0, nxt, aa, ab, 0);
+    A.load(cur, k_load);
+    B.load(cur + kOperandBytes, k_load);
+    mma_frags<T>(acc, fa1, fb1);
+    sched_step<M, R, 0, 0>();  // step 3 under the next fragment reads and the loads
+  }
 }
 
 // The two operands of one output tile.
