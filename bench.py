@@ -239,7 +239,7 @@ def run_fused(args) -> dict:
         if ev is not None:
             ev[2].record(stream)
 
-    ms, fwd_ms, step_ms, peak_delta = _time_steps(args, step, stream)
+    ms, fwd_ms, step_ms, peak_delta, sclk = _time_steps(args, step, stream)
     if int(st.item()) != 0:
         raise RuntimeError("dev_status reports invalid labels")
 
@@ -259,6 +259,7 @@ def run_fused(args) -> dict:
         "step_ms_median": step_ms[len(step_ms) // 2],
         "step_ms_min": step_ms[0],
         "step_ms_max": step_ms[-1],
+        "sclk_mhz": sclk,
         "scratch_bytes": ws_bytes,
         "torch_peak_alloc_delta_bytes": int(peak_delta),
         "scratch_frac_of_unfused_logits": scratch_fraction(ws_bytes, N, V),
@@ -302,7 +303,7 @@ def run_single(args) -> dict:
         if ev is not None:
             ev[2].record(stream)
 
-    ms, _, step_ms, peak_delta = _time_steps(args, step, stream)
+    ms, _, step_ms, peak_delta, sclk = _time_steps(args, step, stream)
     if int(st.item()) != 0:
         raise RuntimeError("dev_status reports invalid labels")
     flop_credit = 8.0 * N * V * D
@@ -317,6 +318,7 @@ def run_single(args) -> dict:
         "step_ms_median": step_ms[len(step_ms) // 2],
         "step_ms_min": step_ms[0],
         "step_ms_max": step_ms[-1],
+        "sclk_mhz": sclk,
         "scratch_bytes": ws_bytes,
         "torch_peak_alloc_delta_bytes": int(peak_delta),
         "scratch_frac_of_unfused_logits": scratch_fraction(ws_bytes, N, V),
@@ -360,7 +362,7 @@ def run_ce(args) -> dict:
         if ev is not None:
             ev[2].record(stream)
 
-    ms, fwd_ms, step_ms, peak_delta = _time_steps(args, step, stream)
+    ms, fwd_ms, step_ms, peak_delta, sclk = _time_steps(args, step, stream)
     if int(st.item()) != 0:
         raise RuntimeError("dev_status reports invalid labels")
     bwd_ms = ms - fwd_ms
@@ -379,6 +381,7 @@ def run_ce(args) -> dict:
         "step_ms_median": step_ms[len(step_ms) // 2],
         "step_ms_min": step_ms[0],
         "step_ms_max": step_ms[-1],
+        "sclk_mhz": sclk,
         "torch_peak_alloc_delta_bytes": int(peak_delta),
         "loss": float(loss.item()),
         "roofline": {"kernel": "ce_rows_bwd", "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
@@ -435,7 +438,7 @@ def run_norm(args) -> dict:
         if ev is not None:
             ev[2].record(stream)
 
-    ms, fwd_ms, step_ms, peak_delta = _time_steps(args, step, stream)
+    ms, fwd_ms, step_ms, peak_delta, sclk = _time_steps(args, step, stream)
     bwd_ms = ms - fwd_ms
     fwd_b, bwd_b = norm_bytes(N, D, es, min(N, 512))
     achieved = bwd_b / (bwd_ms * 1e-3) / 1e9
@@ -452,6 +455,7 @@ def run_norm(args) -> dict:
         "step_ms_median": step_ms[len(step_ms) // 2],
         "step_ms_min": step_ms[0],
         "step_ms_max": step_ms[-1],
+        "sclk_mhz": sclk,
         "torch_peak_alloc_delta_bytes": int(peak_delta),
         "roofline": {"kernel": "rms_bwd (+ 2 dgamma passes)", "bound": "hbm", "achieved": achieved,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
@@ -463,12 +467,78 @@ def run_norm(args) -> dict:
     return out
 
 
+def _parse_sclk_mhz(text: str):
+    """The current level of an amdgpu pp_dpm_sclk listing ("1: 1650Mhz *") in MHz, or None."""
+    import re
+    for line in text.splitlines():
+        if line.rstrip().endswith("*"):
+            m = re.search(r"(\d+)\s*mhz", line, re.I)
+            if m:
+                return float(m.group(1))
+    return None
+
+
+def sclk_path():
+    """The pp_dpm_sclk file of cuda:0: the DRM card whose PCI address matches the device's,
+    or the only card that has one; None when it cannot be told (or is not readable)."""
+    import glob
+    import torch
+    cards = [p for p in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")) if os.access(p, os.R_OK)]
+    p = torch.cuda.get_device_properties(0)
+    want = None
+    if all(hasattr(p, a) for a in ("pci_domain_id", "pci_bus_id", "pci_device_id")):
+        want = f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}"
+    for c in cards:
+        if want and os.path.basename(os.path.realpath(os.path.dirname(c))).lower().startswith(want):
+            return c
+    return cards[0] if len(cards) == 1 and want is None else None
+
+
+class SclkSampler:
+    """Reads the shader clock every `period` seconds on a background thread while active
+    (a read of a sysfs text file: no GPU call); summary() gives the median, min and max MHz."""
+
+    def __init__(self, path, period: float = 0.05):
+        import threading
+        self.path, self.period, self.samples = path, period, []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True) if path else None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                with open(self.path) as f:
+                    v = _parse_sclk_mhz(f.read())
+            except OSError:
+                v = None
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self._thread:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread:
+            self._stop.set()
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return {"median": v[len(v) // 2], "min": v[0], "max": v[-1], "samples": len(v),
+                "source": "pp_dpm_sclk current level, sampled every 50 ms over the timed steps"}
+
+
 def _time_steps(args, step, stream):
     """W warmup steps, one step under torch's allocator peak tracking (the library
     allocates nothing, so the peak stays at what is already held), then K timed steps
     with events around each step and around the whole run.  Returns the mean step ms, the
-    mean ms of the first half of each step (the forward), the sorted per-step ms and the
-    allocator peak delta."""
+    mean ms of the first half of each step (the forward), the sorted per-step ms, the
+    allocator peak delta and the shader clock sampled over the timed steps (or None)."""
     import torch
     for _ in range(args.warmup):
         step()
@@ -481,15 +551,16 @@ def _time_steps(args, step, stream):
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record(stream)
-    for k in range(args.steps):
-        step(evs[k])
-    end.record(stream)
-    torch.cuda.synchronize()
+    with SclkSampler(sclk_path()) as clk:
+        start.record(stream)
+        for k in range(args.steps):
+            step(evs[k])
+        end.record(stream)
+        torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
     fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     step_ms = sorted(e[0].elapsed_time(e[2]) for e in evs)
-    return ms, fwd_ms, step_ms, peak_delta
+    return ms, fwd_ms, step_ms, peak_delta, clk.summary()
 
 
 OCCUPANCY_COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT",

@@ -106,3 +106,24 @@ def test_summarize_occupancy(tmp_path):
     assert r["mfma_busy"] == pytest.approx(0.5) and r["mfma_busy_ghz"] == pytest.approx(1.0)
     assert r["lds_active"] == pytest.approx(0.25) and r["lds_bank_conflict"] == pytest.approx(0.01)
     assert r["lds_issue_wait"] == pytest.approx(0.1)
+
+
+def test_parse_sclk():
+    assert bench._parse_sclk_mhz("0: 500Mhz\n1: 1650Mhz *\n2: 2400Mhz\n") == 1650.0
+    assert bench._parse_sclk_mhz("S: 1423MHz *\n") == 1423.0
+    assert bench._parse_sclk_mhz("0: 500Mhz\n1: 2400Mhz\n") is None
+
+
+def test_sclk_sampler_reads_the_current_level(tmp_path):
+    f = tmp_path / "pp_dpm_sclk"
+    f.write_text("0: 500Mhz\n1: 1700Mhz *\n2: 2400Mhz\n")
+    with bench.SclkSampler(str(f), period=0.001) as s:
+        import time
+        t0 = time.time()
+        while len(s.samples) < 3 and time.time() - t0 < 5:
+            time.sleep(0.005)
+    r = s.summary()
+    assert r["median"] == 1700.0 and r["min"] == 1700.0 and r["samples"] >= 3
+    with bench.SclkSampler(None) as s:
+        pass
+    assert s.summary() is None
