@@ -15,7 +15,9 @@
 //     v_mfma_f32_32x32x16_f16, fp32 v_mfma_f32_32x32x2_f32.
 //   * Operands move HBM -> LDS with direct DMA loads (no register staging), into
 //     unpadded LDS rows whose 16-byte chunks are XOR-swizzled so fragment reads are free
-//     of bank conflicts.
+//     of bank conflicts.  The loads of slice k + 2 are issued after slice k's barrier;
+//     with two K-contiguous operands they are interleaved one by one with the last K
+//     step's MFMAs and the next fragment reads, otherwise issued ahead of those MFMAs.
 //   * Operands whose rows are K-contiguous in HBM (H and W for the logits, the dz slab
 //     for dH) are read from LDS with ds_read_b128.  Operands contracted over their row
 //     index (W for dH; H and the slab for dW) are "MN-contiguous": LDS keeps them as they
@@ -37,6 +39,13 @@
 //                 dz = (p - onehot) * g/N_valid, write it to the chunk slab.
 //   bwd_dh        dH[chunk rows] (+)= slab x W[vocab chunk]   (fp32 accumulator)
 //   bwd_dw        dW[vocab chunk] (+)= slab^T x H[token chunk]
+// Single pass (flce_forward_backward with its larger workspace), per token chunk:
+//   label_blocks, label_total   N_valid of the whole call before any chunk's backward.
+//   fwd_tiles<KEEP> the forward tiles, which also keep p~ = exp(z - m) (m the maximum over
+//                 a half tile of 128 vocabulary rows) in the input type, and m.
+//   fwd_combine, bwd_prep       as above, for the chunk's rows.
+//   keep_to_dz    p~ -> dz in place once lse is known (HBM-bound pass over the slab).
+//   bwd_dh        dH of the chunk with K = V in one launch; bwd_dw accumulates dW.
 // Backward runs token chunks outer, vocabulary chunks inner; each output tile has one
 // owner per launch and chunks are visited in a fixed order, so dW's split over tokens
 // (and dH's over vocabulary) is deterministic without atomics.
