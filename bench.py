@@ -75,15 +75,18 @@ def source_digest(path: str = "fused") -> str:
         return code_digest(f.read())
 
 
-def load_traffic(path: str = "fused"):
+def load_traffic(path: str = "fused", workload: str | None = None):
     """HBM bytes per launch of the path's dominant kernel from the committed counter
-    summary, or None when absent or taken on a different kernel source."""
+    summary, or None when absent, taken on a different kernel source, or taken on another
+    workload than `workload` (default: the path's own)."""
     try:
         with open(PATHS[path][2]) as f:
             t = json.load(f)
     except OSError:
         return None
     if t.get("source_digest") != source_digest(path):
+        return None
+    if t.get("workload") != (workload or PATHS[path][1]):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -266,7 +269,7 @@ def run_fused(args) -> dict:
         "loss": float(loss.item()),
         "roofline": {"kernel": "fwd_tiles", "bound": "mfma", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": load_traffic("fused")},
+                     "traffic": load_traffic("fused", cfg.name)},
         "cpu_baseline": None,
     })
     if not args.no_cpu_baseline:
@@ -385,7 +388,7 @@ def run_ce(args) -> dict:
         "torch_peak_alloc_delta_bytes": int(peak_delta),
         "loss": float(loss.item()),
         "roofline": {"kernel": "ce_rows_bwd", "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": load_traffic("ce")},
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": load_traffic("ce", cfg.name)},
         "cpu_baseline": None,
     })
     if not args.no_cpu_baseline:
@@ -459,7 +462,7 @@ def run_norm(args) -> dict:
         "torch_peak_alloc_delta_bytes": int(peak_delta),
         "roofline": {"kernel": "rms_bwd (+ 2 dgamma passes)", "bound": "hbm", "achieved": achieved,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": load_traffic("norm")},
+                     "traffic": load_traffic("norm", cfg.name)},
         "cpu_baseline": None,
     })
     if not args.no_cpu_baseline:

@@ -127,3 +127,15 @@ def test_sclk_sampler_reads_the_current_level(tmp_path):
     with bench.SclkSampler(None) as s:
         pass
     assert s.summary() is None
+
+
+def test_traffic_record_of_another_workload_is_ignored(tmp_path, monkeypatch):
+    """A record taken on the Llama-3 workload does not describe a run on another one."""
+    rec_file = tmp_path / "rec.json"
+    rec_file.write_text(json.dumps({"source_digest": bench.source_digest("fused"), "workload": "llama3",
+                                    "hbm_bytes_per_launch": 5.0}))
+    kernel, wl, _, src = bench.PATHS["fused"]
+    monkeypatch.setitem(bench.PATHS, "fused", (kernel, wl, str(rec_file), src))
+    assert bench.load_traffic("fused") == 5.0
+    assert bench.load_traffic("fused", "llama3") == 5.0
+    assert bench.load_traffic("fused", "llama2") is None
