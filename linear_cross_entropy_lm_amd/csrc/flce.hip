@@ -13,6 +13,9 @@
 //     per slice.  Workgroups are persistent: each walks a list of tiles with one
 //     continuous load pipeline.  bf16 uses v_mfma_f32_32x32x16_bf16, fp16
 //     v_mfma_f32_32x32x16_f16, fp32 v_mfma_f32_32x32x2_f32.
+//   * The plain forward on 16-bit inputs (fwd_tiles16) runs the same tiles, stages and
+//     loads on 16 x 16 x 32 MFMAs (8 x 4 blocks of 16 x 16 per wave), which draw less
+//     power per flop and so keep a higher clock under the chip's power limit.
 //   * Operands move HBM -> LDS with direct DMA loads (no register staging), into
 //     unpadded LDS rows whose 16-byte chunks are XOR-swizzled so fragment reads are free
 //     of bank conflicts.  The loads of slice k + 2 are issued after slice k's barrier;
@@ -28,7 +31,8 @@
 //     sum-exp are in-lane reductions plus one exchange with lane ^ 32.
 //
 // Kernels:
-//   fwd_tiles     Z^T tiles (W x H^T over D); each workgroup keeps a running (max,
+//   fwd_tiles16 / fwd_tiles
+//                 Z^T tiles (W x H^T over D); each workgroup keeps a running (max,
 //                 sum-exp) per token over the vocabulary tiles it owns -> one partial per
 //                 (workgroup, token), and the label logit (compare in the epilogue).
 //   fwd_combine   merge partials per token in fixed order -> lse, row loss; block sums.
@@ -794,6 +798,294 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles(const T* __restrict__ H
   if (t < kTile && n0 + t < N) part[(int64_t)sp * N + n0 + t] = make_float2(m_run, s_run);
 }
 
+// ---------------------------------------------------------------------------------
+// 16 x 16 x 32 MFMA core for the forward tiles of 16-bit inputs.  Same tiles, waves, LDS
+// stages and DMA loads as the 32 x 32 x 16 core above; per wave 8 x 4 blocks of 16 x 16 and
+// two 32-element K steps per slice.  Lane l supplies row (l & 15) of a block and the K
+// elements of 16-byte chunk 4 ks + (l >> 4); its result element acc[i][j][r] is
+// C[kWaveM wm + 16 i + 4 (l >> 4) + r][kWaveN wn + 16 j + (l & 15)].
+// Why a second core: the chip runs these GEMMs at its power limit, and the 16 x 16 x 32
+// MFMA draws less power per flop (MFMAs alone: 84% of the dense peak at 2.05 GHz against
+// 70-74% at 1.6-1.8 GHz for 32 x 32 x 16), so the forward runs at a higher clock; it
+// needs a leaner register schedule than the other core (below) to fit two waves per SIMD.
+// The other kernels stay on the 32 x 32 core, whose epilogue layouts they are written for.
+// ---------------------------------------------------------------------------------
+namespace c16 {
+constexpr int kBM = kWaveM / 16, kBN = kWaveN / 16;  // 8 x 4 blocks per wave
+constexpr int kSteps = 2;                            // 32-element K steps per slice
+
+template <typename T> struct Mfma;
+template <> struct Mfma<u16> {
+  static __device__ __forceinline__ void run(f32x4& c, const u32x4& a, const u32x4& b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                0, 0);
+  }
+};
+template <> struct Mfma<h16> {
+  static __device__ __forceinline__ void run(f32x4& c, const u32x4& a, const u32x4& b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
+                                               0);
+  }
+};
+
+template <typename T> struct KLoad {
+  static_assert(kDmaPerWave % 4 == 0, "swizzle repeats every two loads only for a multiple of 4");
+  u32x4 rsrc;
+  u32 voff[2], row_step;
+  int kc[2];
+  int k_lim;
+  __device__ __forceinline__ KLoad(const T* base, int ld_bytes, int rows_ok, int k_lim_) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int rows = rows_ok < 0 ? 0 : (rows_ok > kTile ? kTile : rows_ok);
+    rsrc = dma_rsrc(base, (u32)rows * (u32)ld_bytes);
+    k_lim = k_lim_;
+    row_step = 8u * (u32)ld_bytes;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int r = 8 * (kDmaPerWave * w + p) + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      kc[p] = c * Elem<T>::kPerChunk;
+      voff[p] = (u32)r * (u32)ld_bytes + (u32)c * 16u;
+    }
+  }
+  __device__ __forceinline__ u32 off(int i, int k0) const {
+    return k0 + kc[i & 1] < k_lim ? voff[i & 1] + (u32)(i & ~1) * row_step + (u32)k0 * (u32)sizeof(T) : kOOB;
+  }
+  __device__ __forceinline__ void load(char* op, int k0) const {
+#pragma unroll
+    for (int i = 0; i < kDmaPerWave; ++i) dma_one(rsrc, op, off(i, k0), i);
+  }
+  __device__ __forceinline__ void load_one(char* op, int k0, int i) const { dma_one(rsrc, op, off(i, k0), i); }
+};
+
+// K-contiguous operand in the KTile LDS layout: fragment address per K step.  The swizzle
+// (row >> 1) & 7 is the same for a row and the rows 16 blk further, so one address per step
+// serves every block.
+__device__ __forceinline__ void k_addrs(FragAddr& a, int elem0, int lane) {
+  const int row = elem0 + (lane & 15), sw = (row >> 1) & 7, q = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < kSteps; ++ks) a[ks] = row * kKBytes + 16 * ((4 * ks + q) ^ sw);
+}
+__device__ __forceinline__ u32x4 k_frag(const char* op, const FragAddr& a, int blk, int ks) {
+  return *reinterpret_cast<const u32x4*>(op + a[ks] + blk * 16 * kKBytes);
+}
+
+// Row-ring schedule.  A slice is 16 rows (two K steps of 8 rows of kBN products).  Row r
+// multiplies fa[r & 3] (A block r % 8 at step r / 8) by the step's B fragments; A fragments
+// are read three rows ahead into the slot the previous row freed.  The barrier follows row
+// 13 (its fence also waits for the last reads of `cur`, issued in row 12); rows 14-15 issue
+// the DMA loads of the slice after next into `cur` and read the next slice's first A rows
+// and step-0 B fragments from `nxt`.
+constexpr int kRows = kSteps * kBM;  // 16
+static_assert(kDmaPerWave == kBN, "rows 14-15 pair each product with one DMA load");
+// Rows 0-13 in order: each row's kBN products, then its reads (the A fragment three rows
+// ahead; in rows 0-3 also one B fragment of step 1).
+template <int R = 0>
+__device__ __forceinline__ void sched_pre_barrier() {
+  if constexpr (R < 14) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, kBN, 0);
+    constexpr int reads = (R + 3 < kRows ? 1 : 0) + (R < kBN ? 1 : 0);
+    if constexpr (reads > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, reads, 0);
+    sched_pre_barrier<R + 1>();
+  }
+}
+template <typename T, typename TA, typename TB, int R>
+__device__ __forceinline__ void ring_row(f32x4 (&acc)[kBM][kBN], u32x4 (&fa)[4], u32x4 (&fb0)[kBN],
+                                         u32x4 (&fb1)[kBN], char* cur, const char* nxt, const TA& A, const TB& B,
+                                         const FragAddr& aa, const FragAddr& ab, int k_load) {
+  if constexpr (R < 14) {
+    constexpr int step = R / kBM, i = R % kBM;
+#pragma unroll
+    for (int j = 0; j < kBN; ++j) {
+      if constexpr (step == 0)
+        Mfma<T>::run(acc[i][j], fa[R & 3], fb0[j]);
+      else
+        Mfma<T>::run(acc[i][j], fa[R & 3], fb1[j]);
+    }
+    if constexpr (R + 3 < kRows) fa[(R + 3) & 3] = k_frag(cur, aa, (R + 3) % kBM, (R + 3) / kBM);
+    if constexpr (R < kBN) fb1[R] = k_frag(cur + kOperandBytes, ab, R, 1);
+    ring_row<T, TA, TB, R + 1>(acc, fa, fb0, fb1, cur, nxt, A, B, aa, ab, k_load);
+  } else if constexpr (R == 14) {
+    sched_pre_barrier();
+    __builtin_amdgcn_s_setprio(0);
+    dma_barrier();
+    __builtin_amdgcn_s_setprio(1);
+    // The next slice's step-0 B fragments and its A rows 0 and 1 (slots of rows 12 and 13).
+#pragma unroll
+    for (int j = 0; j < kBN; ++j) fb0[j] = k_frag(nxt + kOperandBytes, ab, j, 0);
+    fa[0] = k_frag(nxt, aa, 0, 0);
+    fa[1] = k_frag(nxt, aa, 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // Rows 14 and 15, each product followed by one DMA load of the slice after next.
+#pragma unroll
+    for (int j = 0; j < kBN; ++j) {
+      Mfma<T>::run(acc[6][j], fa[2], fb1[j]);
+      A.load_one(cur, k_load, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    fa[2] = k_frag(nxt, aa, 2, 0);  // row 14 has issued its products
+#pragma unroll
+    for (int j = 0; j < kBN; ++j) {
+      Mfma<T>::run(acc[7][j], fa[3], fb1[j]);
+      B.load_one(cur + kOperandBytes, k_load, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+template <typename AccT> __device__ __forceinline__ void zero_acc(AccT& acc) {
+#pragma unroll
+  for (int i = 0; i < kBM; ++i)
+#pragma unroll
+    for (int j = 0; j < kBN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+template <typename T, typename MakeOps, typename Epi>
+__device__ __forceinline__ void gemm_run(char* lds, int count, int ktiles, const MakeOps& mk, Epi&& epi) {
+  using O = decltype(mk(0));
+  constexpr int BK = kStageK<T>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  FragAddr aa, ab;
+  k_addrs(aa, (wave / kWavesN) * kWaveM, lane);
+  k_addrs(ab, (wave % kWavesN) * kWaveN, lane);
+  f32x4 acc[kBM][kBN];
+  zero_acc(acc);
+  u32x4 fa[4], fb0[kBN], fb1[kBN];
+  char* s0 = lds;
+  char* s1 = lds + kStageBytes;
+  O ld = mk(0);
+  int lt = 0, lk = 0;
+  auto advance = [&]() {
+    if (++lk == ktiles && lt + 1 < count) {
+      lk = 0;
+      ld = mk(++lt);
+    }
+  };
+  ld.a.load(s0, 0);
+  ld.b.load(s0 + kOperandBytes, 0);
+  advance();
+  ld.a.load(s1, lk * BK);
+  ld.b.load(s1 + kOperandBytes, lk * BK);
+  advance();
+  dma_barrier();
+#pragma unroll
+  for (int r = 0; r < 3; ++r) fa[r] = k_frag(s0, aa, r, 0);
+#pragma unroll
+  for (int j = 0; j < kBN; ++j) fb0[j] = k_frag(s0 + kOperandBytes, ab, j, 0);
+  for (int t = 0; t < count; ++t) {
+    for (int k = 0; k < ktiles; k += 2) {
+      ring_row<T, typename O::TA, typename O::TB, 0>(acc, fa, fb0, fb1, s0, s1, ld.a, ld.b, aa, ab, lk * BK);
+      advance();
+      ring_row<T, typename O::TA, typename O::TB, 0>(acc, fa, fb0, fb1, s1, s0, ld.a, ld.b, aa, ab, lk * BK);
+      advance();
+    }
+    epi(t, acc);
+    zero_acc(acc);
+  }
+  __builtin_amdgcn_s_setprio(0);
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+}
+}  // namespace c16
+
+// The forward tiles of fwd_tiles<T, false> on the 16 x 16 x 32 core (16-bit T).
+template <typename T>
+__global__ __launch_bounds__(kThreads, 1) void fwd_tiles16(const T* __restrict__ H, const T* __restrict__ W,
+                                                            const int64_t* __restrict__ y, int N, int D, int V,
+                                                            int n_tiles_n, int splits, float2* __restrict__ part,
+                                                            float* __restrict__ zlab) {
+  using c16::kBM;
+  using c16::kBN;
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes + kRedBytes];
+  const int nt = blockIdx.x % n_tiles_n, sp = blockIdx.x / n_tiles_n;
+  const int n_vt = (V + kTile - 1) / kTile;
+  const int count = (n_vt - sp + splits - 1) / splits;
+  const int n0 = nt * kTile;
+  const int ldb = D * (int)sizeof(T);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, t = threadIdx.x;
+  const int wm = wave / kWavesN, wn = wave % kWavesN, lc = lane & 15, lq = lane >> 4;
+  float2* red = reinterpret_cast<float2*>(lds + kLdsBytes);  // [wm][token in tile]
+  int lab[kBN];  // the column's label when in [0, V), else -1
+#pragma unroll
+  for (int j = 0; j < kBN; ++j) {
+    const int n = n0 + wn * kWaveN + 16 * j + lc;
+    const int64_t yl = n < N ? y[n] : -1;
+    lab[j] = yl >= 0 && yl < V ? (int)yl : -1;
+  }
+  float m_run = -__builtin_inff(), s_run = 0.f;
+
+  auto mk = [&](int i) {
+    const int v0 = (sp + i * splits) * kTile;
+    return Ops<c16::KLoad<T>, c16::KLoad<T>>{c16::KLoad<T>(W + (int64_t)v0 * D, ldb, V - v0, D),
+                                             c16::KLoad<T>(H + (int64_t)n0 * D, ldb, N - n0, D)};
+  };
+  auto epi = [&](int i, const f32x4 (&acc)[kBM][kBN]) {
+    const int v0 = (sp + i * splits) * kTile;
+    const int vbase = v0 + wm * kWaveM + 4 * lq;  // vocab row of acc[0][j][0] in this lane
+    const int vlim = V - vbase;
+    const bool full = v0 + kTile <= V;
+    float mrow[kBN], srow[kBN];
+#pragma unroll
+    for (int j = 0; j < kBN; ++j) {
+      const int n = n0 + wn * kWaveN + 16 * j + lc;
+      float m = -__builtin_inff();
+      if (full) {
+#pragma unroll
+        for (int ii = 0; ii < kBM; ++ii)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) m = fmaxf(m, acc[ii][j][r]);
+      } else {
+#pragma unroll
+        for (int ii = 0; ii < kBM; ++ii)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (16 * ii + r < vlim) m = fmaxf(m, acc[ii][j][r]);
+      }
+      float sum = 0.f;
+      if (m != -__builtin_inff()) {
+        const float mb = m * kLog2e;
+        if (full) {
+#pragma unroll
+          for (int ii = 0; ii < kBM; ++ii)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sum += hw_exp2(__builtin_fmaf(acc[ii][j][r], kLog2e, -mb));
+        } else {
+#pragma unroll
+          for (int ii = 0; ii < kBM; ++ii)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (16 * ii + r < vlim) sum += hw_exp2(__builtin_fmaf(acc[ii][j][r], kLog2e, -mb));
+        }
+      }
+      lse_merge(m, sum, __shfl_xor(m, 16), __shfl_xor(sum, 16));
+      lse_merge(m, sum, __shfl_xor(m, 32), __shfl_xor(sum, 32));
+      // The lane's rows are the offsets 16 ii + r (r < 4) from vbase.
+      const int rel = lab[j] - vbase;
+      if (lab[j] >= 0 && rel >= 0 && rel < kWaveM && (rel & 12) == 0) {
+        float zl = 0.f;
+#pragma unroll
+        for (int ii = 0; ii < kBM; ++ii)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (rel == 16 * ii + r) zl = acc[ii][j][r];
+        zlab[n] = zl;
+      }
+      mrow[j] = m;
+      srow[j] = sum;
+    }
+    if (lq == 0) {
+#pragma unroll
+      for (int j = 0; j < kBN; ++j) red[wm * kTile + wn * kWaveN + 16 * j + lc] = make_float2(mrow[j], srow[j]);
+    }
+    __syncthreads();
+    if (t < kTile) {
+      lse_merge(m_run, s_run, red[t].x, red[t].y);
+      lse_merge(m_run, s_run, red[kTile + t].x, red[kTile + t].y);
+    }
+  };
+  c16::gemm_run<T>(lds, count, even_slices<T>(D), mk, epi);
+  if (t < kTile && n0 + t < N) part[(int64_t)sp * N + n0 + t] = make_float2(m_run, s_run);
+}
+
 __global__ __launch_bounds__(256) void fwd_combine(const float2* __restrict__ part, int n_part,
                                                    const float* __restrict__ zlab, const int64_t* __restrict__ y,
                                                    int N, int V, int64_t ignore_index, float* __restrict__ lse,
@@ -1413,8 +1705,12 @@ flce_status forward_impl(const T* H, const T* W, const int64_t* y, int N, int D,
   int* bbad = reinterpret_cast<int*>(ws + L.bbad);
   const int ntn = (int)ceil_div(N, kTile);
   (void)hipGetLastError();
-  fwd_tiles<T, false><<<dim3((unsigned)ntn * (unsigned)L.splits), dim3(kThreads), 0, s>>>(
-      H, W, y, N, D, V, ntn, L.splits, part, zlab, nullptr, 0, nullptr, 0);
+  if constexpr (sizeof(T) == 2)
+    fwd_tiles16<T><<<dim3((unsigned)ntn * (unsigned)L.splits), dim3(kThreads), 0, s>>>(H, W, y, N, D, V, ntn,
+                                                                                       L.splits, part, zlab);
+  else
+    fwd_tiles<T, false><<<dim3((unsigned)ntn * (unsigned)L.splits), dim3(kThreads), 0, s>>>(
+        H, W, y, N, D, V, ntn, L.splits, part, zlab, nullptr, 0, nullptr, 0);
   fwd_combine<<<dim3(L.nblk), dim3(256), 0, s>>>(part, L.splits, zlab, y, N, V, ignore_index, lse, bloss, bcnt, bbad);
   fwd_finalize<<<dim3(1), dim3(256), 0, s>>>(bloss, bcnt, bbad, L.nblk, loss, n_valid, dev_status);
   return launched();
