@@ -21,7 +21,7 @@ against the HBM peak (8 TB/s), 2 V es + 12 bytes per row (ce_row_bytes).
 
 value        tokens per second (N / mean step time over the timed steps), the whole job
              on one GPU; per-step median/min/max from events around each step
-roofline     the forward logit kernel (fwd_tiles): 2*N*V*D flop per launch over its
+roofline     the forward logit kernel (fwd_tiles16; fwd_tiles for fp32): 2*N*V*D flop per launch over its
              average duration from HIP events on the launch stream, against the bf16
              dense MFMA peak (2.5 PFLOP/s); traffic from the committed rocprofv3 counter
              summary when it matches the current kernel source, else null
@@ -267,7 +267,8 @@ def run_fused(args) -> dict:
         "torch_peak_alloc_delta_bytes": int(peak_delta),
         "scratch_frac_of_unfused_logits": scratch_fraction(ws_bytes, N, V),
         "loss": float(loss.item()),
-        "roofline": {"kernel": "fwd_tiles", "bound": "mfma", "achieved": achieved,
+        "roofline": {"kernel": "fwd_tiles" if cfg.dtype == "f32" else "fwd_tiles16", "bound": "mfma",
+                     "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": load_traffic("fused", cfg.name)},
         "cpu_baseline": None,

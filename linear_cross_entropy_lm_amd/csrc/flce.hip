@@ -13,9 +13,10 @@
 //     per slice.  Workgroups are persistent: each walks a list of tiles with one
 //     continuous load pipeline.  bf16 uses v_mfma_f32_32x32x16_bf16, fp16
 //     v_mfma_f32_32x32x16_f16, fp32 v_mfma_f32_32x32x2_f32.
-//   * The plain forward on 16-bit inputs (fwd_tiles16) runs the same tiles, stages and
-//     loads on 16 x 16 x 32 MFMAs (8 x 4 blocks of 16 x 16 per wave), which draw less
-//     power per flop and so keep a higher clock under the chip's power limit.
+//   * The plain forward and the dz recompute on 16-bit inputs (fwd_tiles16, bwd_dz16) run
+//     the same tiles, stages and loads on 16 x 16 x 32 MFMAs (8 x 4 blocks of 16 x 16 per
+//     wave), which draw less power per flop and so keep a higher clock under the chip's
+//     power limit.
 //   * Operands move HBM -> LDS with direct DMA loads (no register staging), into
 //     unpadded LDS rows whose 16-byte chunks are XOR-swizzled so fragment reads are free
 //     of bank conflicts.  The loads of slice k + 2 are issued after slice k's barrier;
@@ -39,7 +40,8 @@
 //   fwd_finalize  fixed-order sum of block sums -> loss, N_valid, dev_status.
 //   bwd_prep      per row: c = g/N_valid (0 for ignored rows), the slab scale a (|c|, or 2^14
 //                 for fp16) as e2 = lse log2(e) - log2(a) and sign(c) a, label.
-//   bwd_dz        recompute a Z^T tile of one (vocab chunk, token chunk), form
+//   bwd_dz16 / bwd_dz
+//                 recompute a Z^T tile of one (vocab chunk, token chunk), form
 //                 dz = (p - onehot) * g/N_valid, write it to the chunk slab.
 //   bwd_dh        dH[chunk rows] (+)= slab x W[vocab chunk]   (fp32 accumulator)
 //   bwd_dw        dW[vocab chunk] (+)= slab^T x H[token chunk]
@@ -799,16 +801,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles(const T* __restrict__ H
 }
 
 // ---------------------------------------------------------------------------------
-// 16 x 16 x 32 MFMA core for the forward tiles of 16-bit inputs.  Same tiles, waves, LDS
+// 16 x 16 x 32 MFMA core for the 16-bit kernels whose two operands are K-contiguous (the
+// forward tiles and bwd_dz).  Same tiles, waves, LDS
 // stages and DMA loads as the 32 x 32 x 16 core above; per wave 8 x 4 blocks of 16 x 16 and
 // two 32-element K steps per slice.  Lane l supplies row (l & 15) of a block and the K
 // elements of 16-byte chunk 4 ks + (l >> 4); its result element acc[i][j][r] is
 // C[kWaveM wm + 16 i + 4 (l >> 4) + r][kWaveN wn + 16 j + (l & 15)].
 // Why a second core: the chip runs these GEMMs at its power limit, and the 16 x 16 x 32
 // MFMA draws less power per flop (MFMAs alone: 84% of the dense peak at 2.05 GHz against
-// 70-74% at 1.6-1.8 GHz for 32 x 32 x 16), so the forward runs at a higher clock; it
+// 70-74% at 1.6-1.8 GHz for 32 x 32 x 16), so these kernels run at a higher clock; it
 // needs a leaner register schedule than the other core (below) to fit two waves per SIMD.
-// The other kernels stay on the 32 x 32 core, whose epilogue layouts they are written for.
+// The keep forward, bwd_dh and bwd_dw stay on the 32 x 32 core.
 // ---------------------------------------------------------------------------------
 namespace c16 {
 constexpr int kBM = kWaveM / 16, kBN = kWaveN / 16;  // 8 x 4 blocks per wave
@@ -1319,6 +1322,78 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dz(const T* __restrict__ H, c
   gemm_run<T>(lds, my_tile_count(tiles), even_slices<T>(D), mk, epi);
 }
 
+// bwd_dz on the 16 x 16 x 32 core (16-bit T): same tiles, order and slab layout.  A lane
+// holds four consecutive vocabulary rows of one token per 16-row block, so each block
+// becomes one 8-byte store.
+template <typename T>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dz16(const T* __restrict__ H, const T* __restrict__ W, int D,
+                                                         int v0c, int vc_act, int t0c, int tc_act, int n_tiles_t,
+                                                         const float* __restrict__ e2, const float* __restrict__ coef,
+                                                         const int* __restrict__ lab, T* __restrict__ slab,
+                                                         int ld_slab) {
+  using c16::kBM;
+  using c16::kBN;
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  const int ldb = D * (int)sizeof(T);
+  const int tiles = ((vc_act + kTile - 1) / kTile) * n_tiles_t;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / kWavesN, wn = wave % kWavesN, lc = lane & 15, lq = lane >> 4;
+  const int n_vt = (vc_act + kTile - 1) / kTile;
+  auto mk = [&](int i) {
+    int vt, tt;
+    tile_rc(my_tile(i), n_vt, n_tiles_t, vt, tt);
+    const int vl0 = vt * kTile, tl0 = tt * kTile;
+    return Ops<c16::KLoad<T>, c16::KLoad<T>>{c16::KLoad<T>(W + (int64_t)(v0c + vl0) * D, ldb, vc_act - vl0, D),
+                                             c16::KLoad<T>(H + (int64_t)(t0c + tl0) * D, ldb, tc_act - tl0, D)};
+  };
+  auto epi = [&](int i, const f32x4 (&acc)[kBM][kBN]) {
+    int vt, tt;
+    tile_rc(my_tile(i), n_vt, n_tiles_t, vt, tt);
+    const int vl0 = vt * kTile, tl0 = tt * kTile;
+    const int vb = vl0 + wm * kWaveM + 4 * lq;  // chunk-local vocab row of acc[0][j][0]
+    const int vlim = vc_act - vb;
+    const bool full = vl0 + kTile <= vc_act;  // workgroup-uniform: no row past the chunk
+#pragma unroll
+    for (int j = 0; j < kBN; ++j) {
+      const int nl = tl0 + wn * kWaveN + 16 * j + lc;
+      float L2 = __builtin_inff(), cf = 0.f;  // rows past the chunk: exp2(-inf) = 0
+      int rel = -1;
+      if (nl < tc_act) {
+        const int n = t0c + nl;
+        L2 = e2[n];
+        cf = coef[n];
+        const int lb = lab[n];
+        rel = lb < 0 ? -1 : lb - v0c - vb;
+      }
+      const u32 sgn = __builtin_bit_cast(u32, cf) & 0x80000000u;
+      T* out = slab + (int64_t)nl * ld_slab + vb;
+#pragma unroll
+      for (int ii = 0; ii < kBM; ++ii) {
+        float d[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = hw_exp2(__builtin_fmaf(acc[ii][j][e], kLog2e, -L2));
+          d[e] = full || 16 * ii + e < vlim ? p : 0.f;
+        }
+        store4_signed<T>(out + 16 * ii, d, sgn);
+      }
+      // The one-hot term: the lane holding the label's row (offsets 16 ii + e, e < 4)
+      // rewrites that element as (p - 1) cf after the plain store above.
+      if (rel >= 0 && rel < kWaveM && (rel & 12) == 0) {
+        float z = 0.f;
+#pragma unroll
+        for (int ii = 0; ii < kBM; ++ii)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (rel == 16 * ii + e) z = acc[ii][j][e];
+        const float pc = __builtin_bit_cast(float, __builtin_bit_cast(u32, hw_exp2(__builtin_fmaf(z, kLog2e, -L2))) ^ sgn);
+        out[rel] = from_f32<T>(pc - cf);
+      }
+    }
+  };
+  c16::gemm_run<T>(lds, my_tile_count(tiles), even_slices<T>(D), mk, epi);
+}
+
 template <typename TO> __device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, u32 off, float v);
 template <> __device__ __forceinline__ void bstore<float>(__amdgpu_buffer_rsrc_t r, u32 off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(u32, v), r, (int)off, 0, 0);
@@ -1751,8 +1826,12 @@ flce_status backward_impl(const T* H, const T* W, const int64_t* y, const float*
       const int v1c = (int)((vi + 1) * v_tiles / n_vc * kTile);
       const int vc_act = (v1c < V ? v1c : V) - v0c;
       const int n_vt = (int)ceil_div(vc_act, kTile);
-      bwd_dz<T><<<dim3(grid(n_vt * n_tt)), dim3(kThreads), 0, s>>>(H, W, D, v0c, vc_act, t0c, tc_act, n_tt, e2,
-                                                                   coef, lab, slab, ld_slab);
+      if constexpr (sizeof(T) == 2)
+        bwd_dz16<T><<<dim3(grid(n_vt * n_tt)), dim3(kThreads), 0, s>>>(H, W, D, v0c, vc_act, t0c, tc_act, n_tt,
+                                                                       e2, coef, lab, slab, ld_slab);
+      else
+        bwd_dz<T><<<dim3(grid(n_vt * n_tt)), dim3(kThreads), 0, s>>>(H, W, D, v0c, vc_act, t0c, tc_act, n_tt, e2,
+                                                                     coef, lab, slab, ld_slab);
       const dim3 gh(grid(n_tt * n_td)), gw(grid(n_vt * n_td)), blk(kThreads);
       const bool acc_dh = vi > 0, fin = dacc && vi == n_vc - 1;
       if (!acc_dh && !fin)
