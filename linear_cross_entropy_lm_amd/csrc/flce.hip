@@ -13,10 +13,10 @@
 //     per slice.  Workgroups are persistent: each walks a list of tiles with one
 //     continuous load pipeline.  bf16 uses v_mfma_f32_32x32x16_bf16, fp16
 //     v_mfma_f32_32x32x16_f16, fp32 v_mfma_f32_32x32x2_f32.
-//   * The plain forward and the dz recompute on 16-bit inputs (fwd_tiles16, bwd_dz16) run
-//     the same tiles, stages and loads on 16 x 16 x 32 MFMAs (8 x 4 blocks of 16 x 16 per
-//     wave), which draw less power per flop and so keep a higher clock under the chip's
-//     power limit.
+//   * The forward (plain and keep) and the dz recompute on 16-bit inputs (fwd_tiles16,
+//     bwd_dz16) run the same tiles, stages and loads on 16 x 16 x 32 MFMAs (8 x 4 blocks
+//     of 16 x 16 per wave), which draw less power per flop and so keep a higher clock under
+//     the chip's power limit.
 //   * Operands move HBM -> LDS with direct DMA loads (no register staging), into
 //     unpadded LDS rows whose 16-byte chunks are XOR-swizzled so fragment reads are free
 //     of bank conflicts.  The loads of slice k + 2 are issued after slice k's barrier;
@@ -47,7 +47,7 @@
 //   bwd_dw        dW[vocab chunk] (+)= slab^T x H[token chunk]
 // Single pass (flce_forward_backward with its larger workspace), per token chunk:
 //   label_blocks, label_total   N_valid of the whole call before any chunk's backward.
-//   fwd_tiles<KEEP> the forward tiles, which also keep p~ = exp(z - m) (m the maximum over
+//   fwd_tiles16<KEEP> / fwd_tiles<KEEP> the forward tiles, which also keep p~ = exp(z - m) (m the maximum over
 //                 a half tile of 128 vocabulary rows) in the input type, and m.
 //   fwd_combine, bwd_prep       as above, for the chunk's rows.
 //   keep_to_dz    p~ -> dz in place once lse is known (HBM-bound pass over the slab).
@@ -802,7 +802,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles(const T* __restrict__ H
 
 // ---------------------------------------------------------------------------------
 // 16 x 16 x 32 MFMA core for the 16-bit kernels whose two operands are K-contiguous (the
-// forward tiles and bwd_dz).  Same tiles, waves, LDS
+// forward tiles, plain and keep, and bwd_dz).  Same tiles, waves, LDS
 // stages and DMA loads as the 32 x 32 x 16 core above; per wave 8 x 4 blocks of 16 x 16 and
 // two 32-element K steps per slice.  Lane l supplies row (l & 15) of a block and the K
 // elements of 16-byte chunk 4 ks + (l >> 4); its result element acc[i][j][r] is
@@ -811,7 +811,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles(const T* __restrict__ H
 // MFMA draws less power per flop (MFMAs alone: 84% of the dense peak at 2.05 GHz against
 // 70-74% at 1.6-1.8 GHz for 32 x 32 x 16), so these kernels run at a higher clock; it
 // needs a leaner register schedule than the other core (below) to fit two waves per SIMD.
-// The keep forward, bwd_dh and bwd_dw stay on the 32 x 32 core.
+// bwd_dh and bwd_dw, whose transposed operands would need two transposing reads per
+// 16 x 16 fragment, stay on the 32 x 32 core.
 // ---------------------------------------------------------------------------------
 namespace c16 {
 constexpr int kBM = kWaveM / 16, kBN = kWaveN / 16;  // 8 x 4 blocks per wave
@@ -990,16 +991,25 @@ __device__ __forceinline__ void gemm_run(char* lds, int count, int ktiles, const
 }
 }  // namespace c16
 
-// The forward tiles of fwd_tiles<T, false> on the 16 x 16 x 32 core (16-bit T).
-template <typename T>
+// The forward tiles of fwd_tiles<T, KEEP> on the 16 x 16 x 32 core (16-bit T).  With KEEP a
+// lane's four rows of each 16-row block are one 8-byte store of p~, and the 128-row maximum
+// is taken over the four lanes l, l ^ 16, l ^ 32, l ^ 48 that share the token.
+template <typename T, bool KEEP>
 __global__ __launch_bounds__(kThreads, 1) void fwd_tiles16(const T* __restrict__ H, const T* __restrict__ W,
                                                             const int64_t* __restrict__ y, int N, int D, int V,
                                                             int n_tiles_n, int splits, float2* __restrict__ part,
-                                                            float* __restrict__ zlab) {
+                                                            float* __restrict__ zlab, T* __restrict__ keep,
+                                                            int ld_keep, float* __restrict__ mkeep, int ld_mkeep) {
   using c16::kBM;
   using c16::kBN;
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes + kRedBytes];
-  const int nt = blockIdx.x % n_tiles_n, sp = blockIdx.x / n_tiles_n;
+  int nt, sp;
+  if constexpr (KEEP) {
+    tile_rc((int)blockIdx.x, splits, n_tiles_n, sp, nt);
+  } else {
+    nt = blockIdx.x % n_tiles_n;
+    sp = blockIdx.x / n_tiles_n;
+  }
   const int n_vt = (V + kTile - 1) / kTile;
   const int count = (n_vt - sp + splits - 1) / splits;
   const int n0 = nt * kTile;
@@ -1044,23 +1054,45 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles16(const T* __restrict__
             if (16 * ii + r < vlim) m = fmaxf(m, acc[ii][j][r]);
       }
       float sum = 0.f;
-      if (m != -__builtin_inff()) {
-        const float mb = m * kLog2e;
-        if (full) {
+      if constexpr (KEEP) {
+        // The wave's 128-row maximum first, then the exponentials against it, kept and summed.
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        const float mb = (m == -__builtin_inff() ? 0.f : m) * kLog2e;
+        T* out = keep + (int64_t)n * ld_keep + vbase;
 #pragma unroll
-          for (int ii = 0; ii < kBM; ++ii)
+        for (int ii = 0; ii < kBM; ++ii) {
+          float d[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sum += hw_exp2(__builtin_fmaf(acc[ii][j][r], kLog2e, -mb));
-        } else {
-#pragma unroll
-          for (int ii = 0; ii < kBM; ++ii)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (16 * ii + r < vlim) sum += hw_exp2(__builtin_fmaf(acc[ii][j][r], kLog2e, -mb));
+          for (int r = 0; r < 4; ++r) {
+            const float p = hw_exp2(__builtin_fmaf(acc[ii][j][r], kLog2e, -mb));
+            d[r] = full || 16 * ii + r < vlim ? p : 0.f;
+            sum += d[r];
+          }
+          store4<T>(out + 16 * ii, d);
         }
+        sum += __shfl_xor(sum, 16);
+        sum += __shfl_xor(sum, 32);
+        if (lq == 0) mkeep[(int64_t)n * ld_mkeep + (v0 + wm * kWaveM) / 128] = m;
+      } else {
+        if (m != -__builtin_inff()) {
+          const float mb = m * kLog2e;
+          if (full) {
+#pragma unroll
+            for (int ii = 0; ii < kBM; ++ii)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) sum += hw_exp2(__builtin_fmaf(acc[ii][j][r], kLog2e, -mb));
+          } else {
+#pragma unroll
+            for (int ii = 0; ii < kBM; ++ii)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (16 * ii + r < vlim) sum += hw_exp2(__builtin_fmaf(acc[ii][j][r], kLog2e, -mb));
+          }
+        }
+        lse_merge(m, sum, __shfl_xor(m, 16), __shfl_xor(sum, 16));
+        lse_merge(m, sum, __shfl_xor(m, 32), __shfl_xor(sum, 32));
       }
-      lse_merge(m, sum, __shfl_xor(m, 16), __shfl_xor(sum, 16));
-      lse_merge(m, sum, __shfl_xor(m, 32), __shfl_xor(sum, 32));
       // The lane's rows are the offsets 16 ii + r (r < 4) from vbase.
       const int rel = lab[j] - vbase;
       if (lab[j] >= 0 && rel >= 0 && rel < kWaveM && (rel & 12) == 0) {
@@ -1781,8 +1813,8 @@ flce_status forward_impl(const T* H, const T* W, const int64_t* y, int N, int D,
   const int ntn = (int)ceil_div(N, kTile);
   (void)hipGetLastError();
   if constexpr (sizeof(T) == 2)
-    fwd_tiles16<T><<<dim3((unsigned)ntn * (unsigned)L.splits), dim3(kThreads), 0, s>>>(H, W, y, N, D, V, ntn,
-                                                                                       L.splits, part, zlab);
+    fwd_tiles16<T, false><<<dim3((unsigned)ntn * (unsigned)L.splits), dim3(kThreads), 0, s>>>(
+        H, W, y, N, D, V, ntn, L.splits, part, zlab, nullptr, 0, nullptr, 0);
   else
     fwd_tiles<T, false><<<dim3((unsigned)ntn * (unsigned)L.splits), dim3(kThreads), 0, s>>>(
         H, W, y, N, D, V, ntn, L.splits, part, zlab, nullptr, 0, nullptr, 0);
@@ -1954,8 +1986,12 @@ flce_status single_pass_impl(const T* H, const T* W, const int64_t* y, const flo
     const int ntn = (int)ceil_div(rows, kTile);
     const int splits = (int)(kPersistentWGs / ntn < 1 ? 1 : (kPersistentWGs / ntn > L.ld / kTile ? L.ld / kTile
                                                                                                  : kPersistentWGs / ntn));
-    fwd_tiles<T, true><<<dim3((unsigned)(ntn * splits)), dim3(kThreads), 0, s>>>(
-        H + (int64_t)t0 * D, W, y + t0, rows, D, V, ntn, splits, part, zlab, keep, ld, mkeep, ld_m);
+    if constexpr (sizeof(T) == 2)
+      fwd_tiles16<T, true><<<dim3((unsigned)(ntn * splits)), dim3(kThreads), 0, s>>>(
+          H + (int64_t)t0 * D, W, y + t0, rows, D, V, ntn, splits, part, zlab, keep, ld, mkeep, ld_m);
+    else
+      fwd_tiles<T, true><<<dim3((unsigned)(ntn * splits)), dim3(kThreads), 0, s>>>(
+          H + (int64_t)t0 * D, W, y + t0, rows, D, V, ntn, splits, part, zlab, keep, ld, mkeep, ld_m);
     const int blk0 = t0 / 256;
     fwd_combine<<<dim3((unsigned)ceil_div(rows, 256)), dim3(256), 0, s>>>(part, splits, zlab, y + t0, rows, V,
                                                                           ignore_index, lse + t0, bloss + blk0,
