@@ -88,13 +88,17 @@ def test_parity_multi_chunk_backward(dtype):
     _say("errors", err)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("N,D,V", [(1, 256, 1), (1, 64, 300), (65, 128, 1), (63, 512, 257)])
-def test_degenerate_sizes(N, D, V):
-    cfg = I.case(N, D, V, "f32", seed=31, ignore_frac=0.0)
+def test_degenerate_sizes(N, D, V, dtype):
+    """One token, one vocabulary row, a single 64-element K slice (the second slice of the
+    even pair reads nothing), and sizes one short of a tile."""
+    cfg = I.case(N, D, V, dtype, seed=31, ignore_frac=0.0)
     _say("case", cfg.describe())
     inp = I.generate(cfg)
     got = run_gpu(inp)
-    compare(got, _oracle(inp), "f32")
+    assert got["status"] == 0
+    compare(got, _oracle(inp), dtype)
 
 
 def test_all_rows_ignored():

@@ -65,6 +65,8 @@ CASES = [
     ("two_chunks_bf16", I.case(4500, 256, 3000, "bf16", seed=76)),
     ("two_chunks_f16", I.case(4500, 256, 3000, "f16", seed=77)),
     ("V1_f32", I.case(65, 128, 1, "f32", seed=78, ignore_frac=0.0)),
+    ("V1_bf16", I.case(65, 128, 1, "bf16", seed=79, ignore_frac=0.0)),
+    ("N1_D64_f16", I.case(1, 64, 300, "f16", seed=80, ignore_frac=0.0)),
 ]
 
 
