@@ -802,8 +802,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles(const T* __restrict__ H
 
 // ---------------------------------------------------------------------------------
 // 16 x 16 x 32 MFMA core for the 16-bit kernels whose two operands are K-contiguous (the
-// forward tiles, plain and keep, and bwd_dz).  Same tiles, waves, LDS
-// stages and DMA loads as the 32 x 32 x 16 core above; per wave 8 x 4 blocks of 16 x 16 and
+// forward tiles, plain and keep, and bwd_dz).  Same tiles, waves, LDS stages and DMA loads
+// as the 32 x 32 x 16 core above; per wave 8 x 4 blocks of 16 x 16 and
 // two 32-element K steps per slice.  Lane l supplies row (l & 15) of a block and the K
 // elements of 16-byte chunk 4 ks + (l >> 4); its result element acc[i][j][r] is
 // C[kWaveM wm + 16 i + 4 (l >> 4) + r][kWaveN wn + 16 j + (l & 15)].
@@ -811,8 +811,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles(const T* __restrict__ H
 // MFMA draws less power per flop (MFMAs alone: 84% of the dense peak at 2.05 GHz against
 // 70-74% at 1.6-1.8 GHz for 32 x 32 x 16), so these kernels run at a higher clock; it
 // needs a leaner register schedule than the other core (below) to fit two waves per SIMD.
-// bwd_dh and bwd_dw, whose transposed operands would need two transposing reads per
-// 16 x 16 fragment, stay on the 32 x 32 core.
+// bwd_dh and bwd_dw stay on the 32 x 32 core: with their transposed operands (two
+// transposing reads per fragment) this core measured slower, stalled on those reads
+// behind products half as long, below the power limit.
 // ---------------------------------------------------------------------------------
 namespace c16 {
 constexpr int kBM = kWaveM / 16, kBN = kWaveN / 16;  // 8 x 4 blocks per wave
