@@ -1,5 +1,6 @@
 """Write tests/golden/fullsize_<workload>.npz: fp64 oracle values for the full-size
-workloads (Llama-2, Mistral, Llama-3 and Qwen-2.5 shaped heads in bf16, Llama-2 in fp16),
+workloads (Llama-2, Mistral, Llama-3 and Qwen-2.5 shaped heads in bf16, Llama-2 and
+Llama-3 in fp16),
 and for the cross-entropy over materialised Llama-3-shaped logits (ce_llama3).
 
 Only the oracle and the seeded input generator are used.  Stored per workload:
@@ -25,7 +26,7 @@ sys.path.insert(0, os.path.dirname(os.path.dirname(HERE)))
 import oracle  # noqa: E402
 from linear_cross_entropy_lm_amd import inputs as I  # noqa: E402
 
-WORKLOADS = ["llama2", "mistral", "llama3", "qwen25", "llama2_f16", "ce_llama3"]
+WORKLOADS = ["llama2", "mistral", "llama3", "qwen25", "llama2_f16", "llama3_f16", "ce_llama3"]
 
 
 def pick_rows(y: np.ndarray, rng) -> np.ndarray:

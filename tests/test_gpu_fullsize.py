@@ -1,5 +1,5 @@
 """GPU parity at the full workload sizes (Llama-2, Mistral, Llama-3, Qwen-2.5 shaped heads
-in bf16, and the Llama-2 head in fp16), in the launch configuration the benchmark times
+in bf16, and the Llama-2 and Llama-3 heads in fp16), in the launch configuration the benchmark times
 (default workspace and chunking).
 
 Compared against fp64 oracle values stored by tests/golden/make_fullsize_golden.py:
@@ -22,7 +22,7 @@ pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
-@pytest.mark.parametrize("name", ["llama2", "mistral", "llama3", "qwen25", "llama2_f16"])
+@pytest.mark.parametrize("name", ["llama2", "mistral", "llama3", "qwen25", "llama2_f16", "llama3_f16"])
 def test_fullsize_parity(name):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
