@@ -80,3 +80,39 @@ def test_fullsize_parity(name):
     assert abs(lhs - rhs) <= 1e-2 * abs(lhs)
     if name == "llama3":
         assert scratch_fraction(ws_bytes, N, V) <= 0.05
+
+
+@pytest.mark.parametrize("name", ["llama3", "llama3_f16"])
+def test_fullsize_bitwise_deterministic(name):
+    """Two forward + backward runs at the Llama-3 shape give the same bits in loss, lse, dH
+    and dW: every reduction (vocabulary splits, token chunks into dW, vocabulary chunks into
+    dH) runs in a fixed order with no atomics, whatever the scheduling of the workgroups."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from linear_cross_entropy_lm_amd import binding as B
+    cfg = I.CONFIGS[name]
+    print("case", cfg.describe(), flush=True)
+    inp = I.generate(cfg)
+    dev = "cuda:0"
+    H, W, y = inp.device_tensors(dev)
+    N, D, V = cfg.N, cfg.D, cfg.V
+    ws = torch.empty(B.flce_workspace_bytes(N, D, V, H.dtype), dtype=torch.uint8, device=dev)
+    g = torch.tensor([1024.0 if cfg.dtype == "f16" else 1.0], dtype=torch.float32, device=dev)
+    outs = []
+    for _ in range(2):
+        loss = torch.empty(1, dtype=torch.float32, device=dev)
+        lse = torch.empty(N, dtype=torch.float32, device=dev)
+        nv = torch.empty(1, dtype=torch.int32, device=dev)
+        st = torch.empty(1, dtype=torch.int32, device=dev)
+        dH = torch.full_like(H, float("nan"))
+        dW = torch.full((V, D), float("nan"), dtype=torch.float32, device=dev)
+        B.flce_forward(H, W, y, loss, lse, nv, st, ws, -100)
+        B.flce_backward(H, W, y, lse, nv, g, dH, dW, ws, -100)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
+        outs.append((loss, lse, dH, dW))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a.view(torch.int16),
+                           b.view(torch.int32) if b.dtype == torch.float32 else b.view(torch.int16))
+    del outs
+    torch.cuda.empty_cache()
