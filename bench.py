@@ -49,11 +49,11 @@ PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "linear_cross_entropy_lm_amd", "csrc")
 # path -> (dominant kernel, workload, traffic record, kernel source)
 PATHS = {
-    "fused": ("fwd_tiles", "llama3", os.path.join(ROOT, "profiles", "fwd_tiles_llama3_traffic.json"),
+    "fused": ("fwd_tiles16", "llama3", os.path.join(ROOT, "profiles", "fwd_tiles_llama3_traffic.json"),
               os.path.join(CSRC, "flce.hip")),
     "ce": ("ce_rows_bwd", "ce_llama3", os.path.join(ROOT, "profiles", "ce_rows_bwd_ce_llama3_traffic.json"),
            os.path.join(CSRC, "ce_logits.hip")),
-    "single": ("fwd_tiles", "llama3", os.path.join(ROOT, "profiles", "fwd_tiles_keep_llama3_traffic.json"),
+    "single": ("fwd_tiles16", "llama3", os.path.join(ROOT, "profiles", "fwd_tiles_keep_llama3_traffic.json"),
                os.path.join(CSRC, "flce.hip")),
     "norm": ("rms_bwd", "norm_llama3", os.path.join(ROOT, "profiles", "rms_bwd_norm_llama3_traffic.json"),
              os.path.join(CSRC, "rmsnorm.hip")),
