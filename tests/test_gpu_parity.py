@@ -250,3 +250,18 @@ def test_library_allocates_no_device_memory():
     for _ in range(3):
         calls()
     assert torch.cuda.mem_get_info(0)[0] == free0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_labels_in_the_last_partial_vocab_tile(dtype):
+    """Every label in the last seven rows of a ragged vocabulary (1031 = 4 tiles of 256 + 7):
+    the label logit is captured, and the one-hot term subtracted, inside the partial tile
+    whose rows past V are masked."""
+    cfg = I.case(300, 256, 1031, dtype, seed=46, ignore_frac=0.0)
+    inp0 = I.generate(cfg)
+    y = 1024 + torch.arange(300, dtype=torch.int64) % 7
+    y[::11] = -100
+    inp = I.with_labels(inp0, y)
+    got = run_gpu(inp)
+    assert got["status"] == 0
+    _say("errors", compare(got, _oracle(inp), dtype))

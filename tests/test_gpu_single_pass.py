@@ -186,3 +186,18 @@ def test_single_pass_fullsize_llama3(name, ws_factor):
     lhs = (dW.double() * W.double()).sum().item()
     rhs = (dH.double() * H.double()).sum().item()
     assert abs(lhs - rhs) <= 1e-2 * abs(lhs)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_single_pass_labels_in_the_last_partial_vocab_tile(dtype):
+    """As the two-call case: every label in the last seven rows of a 1031-row vocabulary."""
+    cfg = I.case(300, 256, 1031, dtype, seed=81, ignore_frac=0.0)
+    inp0 = I.generate(cfg)
+    y = 1024 + torch.arange(300, dtype=torch.int64) % 7
+    y[::11] = -100
+    inp = I.with_labels(inp0, y)
+    g = 1024.0 if dtype == "f16" else None
+    got = run_fb(inp, g=g)
+    ref = oracle.forward_backward(inp.h64(), inp.w64(), inp.y64(), g=g or 1.0)
+    assert got["status"] == 0
+    compare(got, ref, dtype)
