@@ -45,6 +45,12 @@ CASES = [
     # one row past 16 token tiles (two uneven token chunks) and a ragged 32003-row
     # vocabulary over four vocabulary chunks
     ("odd_NV_bf16", I.case(4097, 256, 32003, "bf16", seed=20)),
+    # the narrowest rows the boundary accepts (one 16-byte chunk, the rest of every K slice
+    # masked) and wide ones (129 K slices of 64, the last one ragged, padded to an even count)
+    ("D8_bf16", I.case(257, 8, 1031, "bf16", seed=22)),
+    ("D8_f32", I.case(257, 8, 1031, "f32", seed=23)),
+    ("D8200_bf16", I.case(300, 8200, 1031, "bf16", seed=24)),
+    ("D8200_f16", I.case(300, 8200, 1031, "f16", seed=25)),
 ]
 
 

@@ -67,6 +67,8 @@ CASES = [
     ("V1_f32", I.case(65, 128, 1, "f32", seed=78, ignore_frac=0.0)),
     ("V1_bf16", I.case(65, 128, 1, "bf16", seed=79, ignore_frac=0.0)),
     ("N1_D64_f16", I.case(1, 64, 300, "f16", seed=80, ignore_frac=0.0)),
+    ("D8_bf16", I.case(257, 8, 1031, "bf16", seed=84)),
+    ("D8200_bf16", I.case(300, 8200, 1031, "bf16", seed=85)),
 ]
 
 
