@@ -912,9 +912,9 @@ __device__ __forceinline__ void ring_row(f32x4 (&acc)[kBM][kBN], u32x4 (&fa)[4],
     ring_row<T, TA, TB, R + 1>(acc, fa, fb0, fb1, cur, nxt, A, B, aa, ab, k_load);
   } else if constexpr (R == 14) {
     sched_pre_barrier();
-    __builtin_amdgcn_s_setprio(0);
+    // No wave-priority change around this barrier (the 32 x 32 core raises it after its
+    // barrier): on this core the two waves of a SIMD ran 0.5% faster at equal priority.
     dma_barrier();
-    __builtin_amdgcn_s_setprio(1);
     // The next slice's step-0 B fragments and its A rows 0 and 1 (slots of rows 12 and 13).
 #pragma unroll
     for (int j = 0; j < kBN; ++j) fb0[j] = k_frag(nxt + kOperandBytes, ab, j, 0);
@@ -987,7 +987,6 @@ __device__ __forceinline__ void gemm_run(char* lds, int count, int ktiles, const
     epi(t, acc);
     zero_acc(acc);
   }
-  __builtin_amdgcn_s_setprio(0);
   __builtin_amdgcn_s_waitcnt(0x0f70);
 }
 }  // namespace c16
