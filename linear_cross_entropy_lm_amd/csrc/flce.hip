@@ -1422,8 +1422,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dz16(const T* __restrict__ H,
 }
 
 template <typename TO> __device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, u32 off, float v);
+// fp32 partials and dW are written (and read back, in tile_out) with the non-temporal
+// policy: each launch touches a tile's 256 KB once, and keeping it out of the L2 leaves the
+// next tile's operand slices there (backward 0.7% faster, single pass 1.4%).  The 16-bit
+// final dH is written in 64-byte half lines, which the non-temporal path would not combine.
+constexpr int kNtAux = 2;
 template <> __device__ __forceinline__ void bstore<float>(__amdgpu_buffer_rsrc_t r, u32 off, float v) {
-  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(u32, v), r, (int)off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(u32, v), r, (int)off, 0, kNtAux);
 }
 template <> __device__ __forceinline__ void bstore<u16>(__amdgpu_buffer_rsrc_t r, u32 off, float v) {
   __builtin_amdgcn_raw_buffer_store_b16((u16)bf16_rne(v), r, (int)off, 0, 0);
@@ -1466,7 +1471,7 @@ __device__ __forceinline__ void tile_out(const f32x16 (&acc)[kBM][kBN], const fl
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const u32 e = col[j] == kOOB ? kOOB : (col[j] + (u32)(32 * i + 8 * (r >> 2) + (r & 3)) * (u32)ld) * 4u;
-          pv[j][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rp, (int)e, 0, 0));
+          pv[j][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rp, (int)e, 0, kNtAux));
         }
     }
 #pragma unroll
