@@ -30,7 +30,11 @@
  *    FLCE_F32: everything is fp32.  The logit gradient dz is rounded to the input type
  *    before the two backward contractions; for fp16, whose range cannot hold dz itself
  *    (about g / N_valid / V), it is held as dz * 2^14 * N_valid / |g| and the factor is
- *    divided out in fp32 after each contraction.
+ *    divided out in fp32 after each contraction.  The fp16 dH output itself is about
+ *    |g| |W| / N_valid per entry: with g = 1 and thousands of valid rows it falls below
+ *    fp16's smallest normal (6.1e-5), where the spacing of subnormals (6e-8) is a visible
+ *    fraction of the value, so fp16 callers scale the loss (g of 2^10 or more at N_valid
+ *    ~ 10^4), as fp16 training does, and divide the gradients by it.
  *  - The caller owns and allocates every buffer, including the workspace (device
  *    scratch).  The library allocates nothing, frees nothing and keeps no state between
  *    calls, so its peak scratch memory is exactly workspace_bytes.
@@ -135,16 +139,36 @@ flce_status flce_backward(const void* H, const void* W, const int64_t* y, const 
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Single-pass workspace: the least bytes flce_forward_backward needs to run without
+ * Single-pass workspace: the least bytes with which flce_forward_backward runs without
  * recomputing the logits.  Token chunks of T = min(N, 4096) rows (rounded up to 256) keep,
  * for the whole vocabulary, p~ = exp(z - m) in the input type (T x V' elements, V' = V
  * rounded up to 256) and the maxima m of each 128-row half tile in fp32 (T x V'/128), plus
- * a few MB of per-row and per-block terms: about T V' es + 4 T V'/128 bytes (1.07 GB, 25%
- * of the 16-bit N x V logit bytes, at N = 16384, V = 128256, bf16).  A larger workspace
- * lets the call take larger chunks (multiples of 4096 rows, up to N): fewer passes of
- * dW's read-modify-write.  0 for invalid sizes.
+ * a few MB of per-row and per-block terms: about T V' es + 4 T V'/128 bytes.  That is far
+ * above the recomputing schedule's workspace: 1.07 GB, 25% of the 16-bit N x V logit
+ * bytes, at N = 16384, V = 128256, bf16, and 102% of them at N = 4096, V = 32000.
+ *
+ * The kernels address operands through 32-bit buffer offsets, which must stay below
+ * 2^31: a token chunk whose kept slab (T x V' x es bytes, read transposed by the dW
+ * contraction) or hidden rows (T x D x es) would pass that is capped to the largest
+ * multiple of 256 rows that fits (at V' es = 304128 bytes, 6912 rows; in fp32 at
+ * V = 152064, 3328 rows).  Where no chunk fits -- the dH contraction reads all of W at
+ * once, so V D es must stay below about 2^31 (e.g. not fp32 with V = 152064, D = 4096,
+ * nor bf16 with V = 152064, D = 8192) -- the single pass is unavailable: this function returns
+ * flce_workspace_bytes(...), and flce_forward_backward takes the recomputing schedule.
+ * 0 for invalid sizes.
  */
 size_t flce_forward_backward_workspace_bytes(int64_t N, int64_t D, int64_t V, int dtype);
+
+/*
+ * The schedule flce_forward_backward takes for a workspace of `workspace_bytes`: writes the
+ * single pass's token chunk to *token_chunk (a multiple of 256; min(N, 4096) rows rounded
+ * up at the least, then multiples of 4096 up to N as the workspace allows, within the cap
+ * above), or 0 when the call runs flce_forward then flce_backward.  Returns
+ * FLCE_ERR_WORKSPACE when neither schedule fits and FLCE_ERR_INVALID_ARG for invalid
+ * sizes or dtype.  Host-only; touches no device.
+ */
+flce_status flce_forward_backward_chunk(int64_t N, int64_t D, int64_t V, int dtype, size_t workspace_bytes,
+                                        int64_t* token_chunk);
 
 /*
  * Forward and backward in one call: loss, lse[N], n_valid, dev_status as flce_forward and
@@ -153,12 +177,13 @@ size_t flce_forward_backward_workspace_bytes(int64_t N, int64_t D, int64_t V, in
  * "Unsloth Architecture: 5x Faster LLM Training via Triton", pillar 1 and its numpy walk
  * through, computes the loss and the hidden-state gradient of a token chunk in one pass
  * over its logits; "Arquitectura interna de Unsloth y optimización en Triton", section 3,
- * backpropagates into H and W directly.  With workspace_bytes >=
- * flce_forward_backward_workspace_bytes(...), each token chunk's logits are computed once
- * (6 N V D flops in all): the logit GEMM keeps p~ and m, the chunk's lse is combined,
- * p~ becomes dz in place, and dH (over the whole vocabulary at once) and dW are contracted
- * from it.  With a smaller workspace (at least flce_workspace_bytes) the call runs
- * flce_forward then flce_backward (8 N V D flops, the logits recomputed).
+ * backpropagates into H and W directly.  When flce_forward_backward_chunk reports a token
+ * chunk for the workspace, each chunk's logits are computed once (6 N V D flops in all):
+ * the logit GEMM keeps p~ and m, the chunk's lse is combined, p~ becomes dz in place, and
+ * dH (over the whole vocabulary at once) and dW are contracted from it.  Otherwise (a
+ * workspace of at least flce_workspace_bytes but below the single pass's, or sizes where
+ * the single pass cannot run) the call runs flce_forward then flce_backward (8 N V D
+ * flops, the logits recomputed).
  *
  * Conventions, alignment, errors and determinism as flce_forward / flce_backward; results
  * of the two schedules agree within rounding (the single pass rounds p~ to the input type
@@ -169,6 +194,42 @@ flce_status flce_forward_backward(const void* H, const void* W, const int64_t* y
                                   float* loss, float* lse, int32_t* n_valid, int32_t* dev_status,
                                   void* dH, float* dW, void* workspace, size_t workspace_bytes,
                                   void* stream);
+
+/*
+ * Launch timing, a measurement aid for benchmarks and profilers (the computation needs none
+ * of it).  Every kernel launch of flce_forward, flce_backward and flce_forward_backward has one
+ * of these ids:
+ */
+enum flce_kernel_id {
+  FLCE_KERNEL_FWD = 0,           /* forward logit tiles with the online log-sum-exp */
+  FLCE_KERNEL_FWD_KEEP = 1,      /* the same, keeping p~ = exp(z - m) (single pass) */
+  FLCE_KERNEL_FWD_COMBINE = 2,   /* merge of the vocabulary splits: lse, row losses */
+  FLCE_KERNEL_FWD_FINALIZE = 3,  /* loss, N_valid, status */
+  FLCE_KERNEL_BWD_PREP = 4,      /* per-row terms of dz */
+  FLCE_KERNEL_DZ = 5,            /* recomputed logit tiles -> dz slab */
+  FLCE_KERNEL_DH = 6,            /* dH partial of the first vocabulary chunk (stored) */
+  FLCE_KERNEL_DH_ACC = 7,        /* dH partial added to the fp32 accumulator */
+  FLCE_KERNEL_DH_FINAL = 8,      /* dH of a single vocabulary chunk, written in the output type */
+  FLCE_KERNEL_DH_ACC_FINAL = 9,  /* last vocabulary chunk: accumulated and written out */
+  FLCE_KERNEL_DW = 10,           /* dW of the first token chunk (stored) */
+  FLCE_KERNEL_DW_ACC = 11,       /* dW of a later token chunk, added in place */
+  FLCE_KERNEL_LABELS = 12,       /* N_valid before any chunk (single pass) */
+  FLCE_KERNEL_KEEP_TO_DZ = 13    /* kept exponentials -> dz slab (single pass) */
+};
+
+/*
+ * flce_timing_begin(events, kernel_ids, capacity): until flce_timing_end, the i-th launch
+ * (i < capacity) carries events[2 i] and events[2 i + 1] -- hipEvent_t handles the caller
+ * created with timing enabled -- as the start and stop events of its own dispatch
+ * (hipExtLaunchKernel: stamped from the launch itself, no marker queued between kernels),
+ * and its flce_kernel_id is written to kernel_ids[i].  Launches past `capacity` run
+ * without events.  Host-global state: one caller at a time, and no calls on other threads
+ * meanwhile.  Returns FLCE_OK, or FLCE_ERR_INVALID_ARG for null arrays or capacity < 1.
+ * flce_timing_end() stops and returns the number of launches recorded; read the events
+ * after synchronising.
+ */
+int32_t flce_timing_begin(void** events, int32_t* kernel_ids, int32_t capacity);
+int32_t flce_timing_end(void);
 
 /* Static, human-readable name of a status code. */
 const char* flce_status_string(int status);

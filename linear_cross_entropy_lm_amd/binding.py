@@ -16,6 +16,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflce.so"
 
 FLCE_OK, FLCE_ERR_INVALID_ARG, FLCE_ERR_ALIGN, FLCE_ERR_WORKSPACE, FLCE_ERR_HIP = range(5)
 FLCE_F32, FLCE_BF16, FLCE_F16 = 0, 1, 2
+# enum flce_kernel_id of include/flce.h
+KERNEL_NAMES = ["fwd", "fwd_keep", "fwd_combine", "fwd_finalize", "bwd_prep", "dz", "dh", "dh_acc", "dh_final",
+                "dh_acc_final", "dw", "dw_acc", "labels", "keep_to_dz"]
 IGNORE_INDEX = -100
 
 # symbol -> (restype, argtypes), in the order of include/flce.h, flce_ce.h, flce_norm.h
@@ -26,8 +29,11 @@ SIGNATURES = {
     "flce_forward": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I32, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
     "flce_backward": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I64, _P, _P, _P, _SZ, _P]),
     "flce_forward_backward_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I32]),
+    "flce_forward_backward_chunk": (_I32, [_I64, _I64, _I64, _I32, _SZ, _P]),
     "flce_forward_backward": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I32, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
                                      _P]),
+    "flce_timing_begin": (_I32, [_P, _P, _I32]),
+    "flce_timing_end": (_I32, []),
     "flce_status_string": (ctypes.c_char_p, [_I32]),
     "flce_ce_workspace_bytes": (_SZ, [_I64]),
     "flce_ce_forward": (_I32, [_P, _I64, _P, _I64, _I64, _I32, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -153,6 +159,17 @@ def flce_forward_backward_workspace_bytes(N: int, D: int, V: int, dtype) -> int:
     return int(lib.flce_forward_backward_workspace_bytes(N, D, V, code))
 
 
+def flce_forward_backward_chunk(N: int, D: int, V: int, dtype, workspace_bytes: int) -> int:
+    """The single pass's token chunk for this workspace, or 0 when flce_forward_backward
+    takes the two-call schedule."""
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    tc = ctypes.c_int64(-1)
+    st = lib.flce_forward_backward_chunk(N, D, V, code, workspace_bytes, ctypes.byref(tc))
+    if st != FLCE_OK:
+        raise FlceError(st, "flce_forward_backward_chunk")
+    return tc.value
+
+
 def flce_forward_backward(H, W, y, grad_loss, loss, lse, n_valid, dev_status, dH, dW, workspace,
                           ignore_index=IGNORE_INDEX, stream=None) -> None:
     """Forward and backward in one call; the single-pass schedule when ``workspace`` holds
@@ -267,12 +284,23 @@ def flce_rmsnorm_backward(X, gamma, rstd, dH, dX, dgamma, workspace, stream=None
         raise FlceError(st, "flce_rmsnorm_backward")
 
 
+def _check_labels(status: torch.Tensor) -> None:
+    """Raise if the forward flagged a label outside [0, V) that is not ignore_index (reads the
+    device status: one synchronisation)."""
+    if int(status.item()) != 0:
+        raise ValueError("labels outside [0, V) that are not ignore_index (the library treated those rows "
+                         "as ignored)")
+
+
 class FusedLinearCrossEntropy(torch.autograd.Function):
     """loss = mean cross-entropy of (H @ W^T, y) with the fused library.  Saves only the
-    per-row lse and N_valid for the backward; dW is returned in fp32."""
+    per-row lse and N_valid for the backward; dW is returned in the weights' dtype.  With
+    check_labels (the default) the forward raises ValueError on a label outside [0, V) that
+    is not ignore_index, at the cost of one synchronisation; without it such rows are
+    treated as ignored."""
 
     @staticmethod
-    def forward(ctx, H, W, y, ignore_index=IGNORE_INDEX):
+    def forward(ctx, H, W, y, ignore_index=IGNORE_INDEX, check_labels=True):
         N, D = H.shape
         V = W.shape[0]
         dev = H.device
@@ -282,6 +310,8 @@ class FusedLinearCrossEntropy(torch.autograd.Function):
         nv = torch.empty(1, dtype=torch.int32, device=dev)
         status = torch.empty(1, dtype=torch.int32, device=dev)
         flce_forward(H, W, y, loss, lse, nv, status, ws, ignore_index)
+        if check_labels:
+            _check_labels(status)
         ctx.save_for_backward(H, W, y, lse, nv)
         ctx.ignore_index = ignore_index
         return loss[0]
@@ -296,21 +326,21 @@ class FusedLinearCrossEntropy(torch.autograd.Function):
         dW = torch.empty(V, D, dtype=torch.float32, device=H.device)
         gl = g.reshape(1).to(torch.float32).contiguous()
         flce_backward(H, W, y, lse, nv, gl, dH, dW, ws, ctx.ignore_index)
-        return dH, dW.to(W.dtype), None, None
+        return dH, dW.to(W.dtype), None, None, None
 
 
-def fused_linear_cross_entropy(H, W, y, ignore_index=IGNORE_INDEX):
-    return FusedLinearCrossEntropy.apply(H, W, y, ignore_index)
+def fused_linear_cross_entropy(H, W, y, ignore_index=IGNORE_INDEX, check_labels=True):
+    return FusedLinearCrossEntropy.apply(H, W, y, ignore_index, check_labels)
 
 
 class NormLinearCrossEntropy(torch.autograd.Function):
     """loss = mean cross-entropy of (RMSNorm(X) * gamma @ W^T, y): the final norm, the lm_head
     and the loss.  Forward saves X, H, rstd, lse and N_valid; the backward's dH feeds the
     norm's backward directly.  dgamma and dW are returned in fp32 cast to the weights'
-    dtype."""
+    dtype.  check_labels as for FusedLinearCrossEntropy."""
 
     @staticmethod
-    def forward(ctx, X, gamma, W, y, eps=0.0, ignore_index=IGNORE_INDEX):
+    def forward(ctx, X, gamma, W, y, eps=0.0, ignore_index=IGNORE_INDEX, check_labels=True):
         N, D = X.shape
         V = W.shape[0]
         dev = X.device
@@ -323,6 +353,8 @@ class NormLinearCrossEntropy(torch.autograd.Function):
         nv = torch.empty(1, dtype=torch.int32, device=dev)
         status = torch.empty(1, dtype=torch.int32, device=dev)
         flce_forward(H, W, y, loss, lse, nv, status, ws, ignore_index)
+        if check_labels:
+            _check_labels(status)
         ctx.save_for_backward(X, gamma, W, y, H, rstd, lse, nv)
         ctx.ignore_index = ignore_index
         return loss[0]
@@ -342,4 +374,4 @@ class NormLinearCrossEntropy(torch.autograd.Function):
         dX = torch.empty_like(X)
         dgamma = torch.empty(D, dtype=torch.float32, device=dev)
         flce_rmsnorm_backward(X, gamma, rstd, dH, dX, dgamma, nws)
-        return dX, dgamma.to(gamma.dtype), dW.to(W.dtype), None, None, None
+        return dX, dgamma.to(gamma.dtype), dW.to(W.dtype), None, None, None, None

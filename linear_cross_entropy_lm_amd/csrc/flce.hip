@@ -56,10 +56,13 @@
 // owner per launch and chunks are visited in a fixed order, so dW's split over tokens
 // (and dH's over vocabulary) is deterministic without atomics.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+
 #include "flce.h"
+#include "flce_plan.h"
 
 namespace {
 
@@ -132,7 +135,9 @@ template <> __device__ __forceinline__ float from_f32<float>(float f) { return f
 // so ragged edges need no branches (masked chunks use the offset kOOB).
 // ---------------------------------------------------------------------------------
 
-constexpr u32 kOOB = 0x7ffffff0u;
+// The masked-chunk sentinel: at or past every descriptor range, since the host accepts a
+// launch only when every offset its operands can form stays at or below this value.
+constexpr u32 kOOB = (u32)flce_plan::kDescLimit;
 constexpr int kDmaBytes = 1024;                                 // one wave-wide DMA load
 constexpr int kDmaPerWave = kOperandBytes / kDmaBytes / (kThreads / 64);  // 4
 
@@ -629,6 +634,8 @@ template <typename T> __device__ __forceinline__ int even_slices(int K) {
 
 // Four consecutive values stored in the element type (defined with the backward epilogues).
 template <typename T> __device__ __forceinline__ void store4(T* p, const float (&d)[4]);
+// Four values in the 16-bit element type, packed for one 8-byte store (round to nearest even).
+template <typename T> __device__ __forceinline__ u32x2 pack4(const float (&d)[4]);
 
 // LDS past the two GEMM stages, for the cross-wave (max, sum-exp) merge.
 constexpr int kRedBytes = 2 * kTile * (int)sizeof(float2);
@@ -988,7 +995,10 @@ __device__ __forceinline__ void gemm_run(char* lds, int count, int ktiles, const
 
 // The forward tiles of fwd_tiles<T, KEEP> on the 16 x 16 x 32 core (16-bit T).  With KEEP a
 // lane's four rows of each 16-row block are one 8-byte store of p~, and the 128-row maximum
-// is taken over the four lanes l, l ^ 16, l ^ 32, l ^ 48 that share the token.
+// is taken over the four lanes l, l ^ 16, l ^ 32, l ^ 48 that share the token.  The token
+// tile's labels and each token's running (max, sum-exp) live in LDS rather than registers:
+// the K loop holds 256 registers per lane, and anything more kept live across it would
+// spill to private memory, which the runtime must then allocate for the dispatch.
 template <typename T, bool KEEP>
 __global__ __launch_bounds__(kThreads, 1) void fwd_tiles16(const T* __restrict__ H, const T* __restrict__ W,
                                                             const int64_t* __restrict__ y, int N, int D, int V,
@@ -997,7 +1007,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles16(const T* __restrict__
                                                             int ld_keep, float* __restrict__ mkeep, int ld_mkeep) {
   using c16::kBM;
   using c16::kBN;
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes + kRedBytes];
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes + kRedBytes + kTile * 12];
   int nt, sp;
   if constexpr (KEEP) {
     tile_rc((int)blockIdx.x, splits, n_tiles_n, sp, nt);
@@ -1009,17 +1019,25 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles16(const T* __restrict__
   const int count = (n_vt - sp + splits - 1) / splits;
   const int n0 = nt * kTile;
   const int ldb = D * (int)sizeof(T);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, t = threadIdx.x;
-  const int wm = wave / kWavesN, wn = wave % kWavesN, lc = lane & 15, lq = lane >> 4;
-  float2* red = reinterpret_cast<float2*>(lds + kLdsBytes);  // [wm][token in tile]
-  int lab[kBN];  // the column's label when in [0, V), else -1
-#pragma unroll
-  for (int j = 0; j < kBN; ++j) {
-    const int n = n0 + wn * kWaveN + 16 * j + lc;
-    const int64_t yl = n < N ? y[n] : -1;
-    lab[j] = yl >= 0 && yl < V ? (int)yl : -1;
+  const int t = threadIdx.x;
+  float2* red = reinterpret_cast<float2*>(lds + kLdsBytes);                  // [wm][token in tile]
+  float2* run = reinterpret_cast<float2*>(lds + kLdsBytes + kRedBytes);      // [token in tile]
+  int* tlab = reinterpret_cast<int*>(lds + kLdsBytes + kRedBytes + kTile * 8);  // [token in tile]
+  // Token t of the tile: its label when in [0, V), else -1, and the running (max, sum-exp)
+  // over this workgroup's vocabulary tiles.  The GEMM's first barrier orders these writes
+  // before any epilogue reads them.
+  if (t < kTile) {
+    const int64_t yl = n0 + t < N ? y[n0 + t] : -1;
+    tlab[t] = yl >= 0 && yl < V ? (int)yl : -1;
+    run[t] = make_float2(-__builtin_inff(), 0.f);
   }
-  float m_run = -__builtin_inff(), s_run = 0.f;
+  // KEEP: the token tile's rows of the kept slab and of the maxima, addressed through buffer
+  // descriptors with 32-bit offsets (the host bounds 256 kept rows below 2^31 bytes), so
+  // the epilogue's store addresses need one register per lane rather than 64-bit pointers.
+  const __amdgpu_buffer_rsrc_t rkeep =
+      make_rsrc(KEEP ? keep + (int64_t)n0 * ld_keep : keep, KEEP ? (u32)kTile * (u32)ld_keep * (u32)sizeof(T) : 0u);
+  const __amdgpu_buffer_rsrc_t rmkeep =
+      make_rsrc(KEEP ? mkeep + (int64_t)n0 * ld_mkeep : mkeep, KEEP ? (u32)kTile * (u32)ld_mkeep * 4u : 0u);
 
   auto mk = [&](int i) {
     const int v0 = (sp + i * splits) * kTile;
@@ -1027,6 +1045,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles16(const T* __restrict__
                                              c16::KLoad<T>(H + (int64_t)n0 * D, ldb, N - n0, D)};
   };
   auto epi = [&](int i, const f32x4 (&acc)[kBM][kBN]) {
+    // The lane's positions, from a copy of the thread index the compiler cannot see through:
+    // every address below is then formed here, per tile, instead of being hoisted out of the
+    // tile loop and kept live (spilled) across the K loop.
+    int tid = (int)threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int wm = (tid >> 6) / kWavesN, wn = (tid >> 6) % kWavesN, lc = tid & 15, lq = (tid & 63) >> 4;
     const int v0 = (sp + i * splits) * kTile;
     const int vbase = v0 + wm * kWaveM + 4 * lq;  // vocab row of acc[0][j][0] in this lane
     const int vlim = V - vbase;
@@ -1054,7 +1078,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles16(const T* __restrict__
         m = fmaxf(m, __shfl_xor(m, 16));
         m = fmaxf(m, __shfl_xor(m, 32));
         const float mb = (m == -__builtin_inff() ? 0.f : m) * kLog2e;
-        T* out = keep + (int64_t)n * ld_keep + vbase;
+        const int nl = wn * kWaveN + 16 * j + lc;  // token row within the tile
+        const u32 out = ((u32)nl * (u32)ld_keep + (u32)vbase) * (u32)sizeof(T);
 #pragma unroll
         for (int ii = 0; ii < kBM; ++ii) {
           float d[4];
@@ -1064,11 +1089,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles16(const T* __restrict__
             d[r] = full || 16 * ii + r < vlim ? p : 0.f;
             sum += d[r];
           }
-          store4<T>(out + 16 * ii, d);
+          __builtin_amdgcn_raw_buffer_store_b64(pack4<T>(d), rkeep, (int)(out + 16u * ii * (u32)sizeof(T)), 0, 0);
         }
         sum += __shfl_xor(sum, 16);
         sum += __shfl_xor(sum, 32);
-        if (lq == 0) mkeep[(int64_t)n * ld_mkeep + (v0 + wm * kWaveM) / 128] = m;
+        if (lq == 0)
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(u32, m), rmkeep,
+                                                (int)(((u32)nl * (u32)ld_mkeep + (u32)((v0 + wm * kWaveM) / 128)) * 4u),
+                                                0, 0);
       } else {
         if (m != -__builtin_inff()) {
           const float mb = m * kLog2e;
@@ -1089,8 +1117,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles16(const T* __restrict__
         lse_merge(m, sum, __shfl_xor(m, 32), __shfl_xor(sum, 32));
       }
       // The lane's rows are the offsets 16 ii + r (r < 4) from vbase.
-      const int rel = lab[j] - vbase;
-      if (lab[j] >= 0 && rel >= 0 && rel < kWaveM && (rel & 12) == 0) {
+      const int labj = tlab[wn * kWaveN + 16 * j + lc];
+      const int rel = labj - vbase;
+      if (labj >= 0 && rel >= 0 && rel < kWaveM && (rel & 12) == 0) {
         float zl = 0.f;
 #pragma unroll
         for (int ii = 0; ii < kBM; ++ii)
@@ -1107,13 +1136,15 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles16(const T* __restrict__
       for (int j = 0; j < kBN; ++j) red[wm * kTile + wn * kWaveN + 16 * j + lc] = make_float2(mrow[j], srow[j]);
     }
     __syncthreads();
-    if (t < kTile) {
-      lse_merge(m_run, s_run, red[t].x, red[t].y);
-      lse_merge(m_run, s_run, red[kTile + t].x, red[kTile + t].y);
+    if (tid < kTile) {
+      float2 r = run[tid];
+      lse_merge(r.x, r.y, red[tid].x, red[tid].y);
+      lse_merge(r.x, r.y, red[kTile + tid].x, red[kTile + tid].y);
+      run[tid] = r;
     }
   };
   c16::gemm_run<T>(lds, count, even_slices<T>(D), mk, epi);
-  if (t < kTile && n0 + t < N) part[(int64_t)sp * N + n0 + t] = make_float2(m_run, s_run);
+  if (t < kTile && n0 + t < N) part[(int64_t)sp * N + n0 + t] = run[t];
 }
 
 __global__ __launch_bounds__(256) void fwd_combine(const float2* __restrict__ part, int n_part,
@@ -1246,6 +1277,12 @@ __device__ __forceinline__ u32 pack_f16x2(float a, float b) {
 }
 template <> __device__ __forceinline__ void store4<h16>(h16* p, const float (&d)[4]) {
   *reinterpret_cast<u32x2*>(p) = u32x2{pack_f16x2(d[0], d[1]), pack_f16x2(d[2], d[3])};
+}
+template <> __device__ __forceinline__ u32x2 pack4<u16>(const float (&d)[4]) {
+  return u32x2{bf16_rne(d[0]) | (bf16_rne(d[1]) << 16), bf16_rne(d[2]) | (bf16_rne(d[3]) << 16)};
+}
+template <> __device__ __forceinline__ u32x2 pack4<h16>(const float (&d)[4]) {
+  return u32x2{pack_f16x2(d[0], d[1]), pack_f16x2(d[2], d[3])};
 }
 
 // store4 of the values with their sign bits xor-ed with sgn (0 or 0x80000000).
@@ -1685,120 +1722,42 @@ __global__ __launch_bounds__(kDzThreads) void keep_to_dz(T* __restrict__ slab, i
 // Host side: argument checks, workspace carving, launch sequences.
 // ---------------------------------------------------------------------------------
 
-constexpr int64_t kMaxDim = (int64_t(1) << 31) - 512;
-constexpr int64_t kMaxHidden = 65536;  // keeps every buffer-descriptor range below 2^31 bytes
-constexpr int64_t kDefaultTokenChunk = 4096;
-constexpr int64_t kDefaultVocabChunk = 8192;
-constexpr int64_t kMinDefaultVocabChunk = 4096;
-
-inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
-inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
-inline size_t region(size_t bytes) { return (size_t)round_up((int64_t)bytes, 256); }
-
-bool sizes_ok(int64_t N, int64_t D, int64_t V, int dtype) {
-  return N >= 1 && D >= 1 && V >= 1 && N <= kMaxDim && D <= kMaxHidden && V <= kMaxDim &&
-         (dtype == FLCE_F32 || dtype == FLCE_BF16 || dtype == FLCE_F16);
-}
-
-size_t elem_size(int dtype) { return dtype == FLCE_F32 ? 4 : 2; }
-
-// Workgroups resident at once: one 512-thread, ~150 KB-LDS workgroup per CU, 256 CUs.
-constexpr int kPersistentWGs = 256;
-
-struct FwdLayout {
-  size_t part, zlab, bloss, bcnt, bbad, total;
-  int splits, nblk;
-};
-
-// Forward: ceil(N / 256) token tiles, each shared by `splits` workgroups that split the
-// vocabulary tiles between them (token tiles x splits ~ the resident workgroups).
-FwdLayout fwd_layout(int64_t N, int64_t V) {
-  FwdLayout L;
-  const int64_t ntn = ceil_div(N, kTile), n_vt = ceil_div(V, kTile);
-  int64_t sp = kPersistentWGs / ntn;
-  sp = sp < 1 ? 1 : (sp > n_vt ? n_vt : sp);
-  L.splits = (int)sp;
-  L.nblk = (int)ceil_div(N, 256);
-  size_t off = 0;
-  L.part = off;
-  off += region((size_t)L.splits * (size_t)N * sizeof(float2));
-  L.zlab = off;
-  off += region((size_t)N * sizeof(float));
-  L.bloss = off;
-  off += region((size_t)L.nblk * sizeof(double));
-  L.bcnt = off;
-  off += region((size_t)L.nblk * sizeof(int));
-  L.bbad = off;
-  off += region((size_t)L.nblk * sizeof(int));
-  L.total = off;
-  return L;
-}
-
-struct BwdLayout {
-  int64_t tc, vc;  // chunk sizes (multiples of 256)
-  size_t e2, coef, lab, oscale, slab, dacc, total;
-};
-
-BwdLayout bwd_layout(int64_t N, int64_t D, int dtype, int64_t tc, int64_t vc) {
-  BwdLayout L;
-  L.tc = tc;
-  L.vc = vc;
-  size_t off = 0;
-  L.e2 = off;
-  off += region((size_t)N * 4);
-  L.coef = off;
-  off += region((size_t)N * 4);
-  L.lab = off;
-  off += region((size_t)N * 4);
-  L.oscale = off;
-  off += region(4);
-  L.slab = off;
-  off += region((size_t)tc * (size_t)vc * elem_size(dtype));
-  L.dacc = off;
-  if (dtype != FLCE_F32) off += region((size_t)tc * (size_t)D * 4);
-  L.total = off;
-  return L;
-}
-
-// Default chunking: token chunk min(N, 4096), vocabulary chunk min(V, 8192), both rounded
-// up to 256; the vocabulary chunk is trimmed in steps of 256 (not below 4096) while the
-// backward workspace exceeds 1/20 of the 16-bit [N, V] logit tensor.
-void default_chunks(int64_t N, int64_t D, int64_t V, int dtype, int64_t* tc_out, int64_t* vc_out) {
-  const int64_t tc = round_up(N < kDefaultTokenChunk ? N : kDefaultTokenChunk, kTile);
-  int64_t vc = round_up(V < kDefaultVocabChunk ? V : kDefaultVocabChunk, kTile);
-  const double cap = 0.05 * 2.0 * (double)N * (double)V;
-  while (vc > kMinDefaultVocabChunk && (double)bwd_layout(N, D, dtype, tc, vc).total > cap) vc -= kTile;
-  *tc_out = tc;
-  *vc_out = vc;
-}
-
-// Largest chunking that fits `ws`, shrinking the larger chunk by halves from the default.
-bool pick_chunks(int64_t N, int64_t D, int64_t V, int dtype, size_t ws, int64_t* tc_out, int64_t* vc_out) {
-  int64_t tc, vc;
-  default_chunks(N, D, V, dtype, &tc, &vc);
-  for (;;) {
-    if (bwd_layout(N, D, dtype, tc, vc).total <= ws) {
-      *tc_out = tc;
-      *vc_out = vc;
-      return true;
-    }
-    if (tc == kTile && vc == kTile) return false;
-    if (vc >= tc && vc > kTile)
-      vc = round_up(vc / 2, kTile);
-    else
-      tc = round_up(tc / 2, kTile);
-  }
-}
-
-size_t default_bwd_bytes(int64_t N, int64_t D, int64_t V, int dtype) {
-  int64_t tc, vc;
-  default_chunks(N, D, V, dtype, &tc, &vc);
-  return bwd_layout(N, D, dtype, tc, vc).total;
-}
+using flce_plan::BwdLayout;
+using flce_plan::FwdLayout;
+using flce_plan::SpLayout;
+using flce_plan::ceil_div;
+using flce_plan::fwd_layout;
+using flce_plan::kPersistentWGs;
+using flce_plan::pick_chunks;
+using flce_plan::sizes_ok;
+static_assert(flce_plan::kTile == kTile && flce_plan::kSliceBytes == kKBytes, "plan and kernels share tile shapes");
+static_assert(flce_plan::kPersistentWGs == 256, "one resident GEMM workgroup per CU");
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 flce_status launched() { return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP; }
+
+// Launch timing (flce_timing_begin / flce_timing_end): while active, each launch takes the
+// next pair of the caller's events as the start and stop events of its own dispatch
+// (hipExtLaunchKernel stamps them from the launch packet; nothing else is queued on the
+// stream) and records its kernel id.  Inactive, launches are plain.
+struct LaunchTiming {
+  hipEvent_t* events = nullptr;
+  int32_t* ids = nullptr;
+  int32_t capacity = 0, count = 0;
+};
+LaunchTiming g_timing;
+
+template <typename... P, typename... A>
+void launch(int id, void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t s, A... args) {
+  if (g_timing.events && g_timing.count < g_timing.capacity) {
+    const int i = g_timing.count++;
+    g_timing.ids[i] = id;
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, g_timing.events[2 * i], g_timing.events[2 * i + 1], 0, args...);
+    return;
+  }
+  kernel<<<grid, block, 0, s>>>(args...);
+}
 
 template <typename T>
 flce_status forward_impl(const T* H, const T* W, const int64_t* y, int N, int D, int V, int64_t ignore_index,
@@ -1813,13 +1772,13 @@ flce_status forward_impl(const T* H, const T* W, const int64_t* y, int N, int D,
   const int ntn = (int)ceil_div(N, kTile);
   (void)hipGetLastError();
   if constexpr (sizeof(T) == 2)
-    fwd_tiles16<T, false><<<dim3((unsigned)ntn * (unsigned)L.splits), dim3(kThreads), 0, s>>>(
+    launch(FLCE_KERNEL_FWD, fwd_tiles16<T, false>, dim3((unsigned)ntn * (unsigned)L.splits), dim3(kThreads), s,
         H, W, y, N, D, V, ntn, L.splits, part, zlab, nullptr, 0, nullptr, 0);
   else
-    fwd_tiles<T, false><<<dim3((unsigned)ntn * (unsigned)L.splits), dim3(kThreads), 0, s>>>(
+    launch(FLCE_KERNEL_FWD, fwd_tiles<T, false>, dim3((unsigned)ntn * (unsigned)L.splits), dim3(kThreads), s,
         H, W, y, N, D, V, ntn, L.splits, part, zlab, nullptr, 0, nullptr, 0);
-  fwd_combine<<<dim3(L.nblk), dim3(256), 0, s>>>(part, L.splits, zlab, y, N, V, ignore_index, lse, bloss, bcnt, bbad);
-  fwd_finalize<<<dim3(1), dim3(256), 0, s>>>(bloss, bcnt, bbad, L.nblk, loss, n_valid, dev_status);
+  launch(FLCE_KERNEL_FWD_COMBINE, fwd_combine, dim3(L.nblk), dim3(256), s, part, L.splits, zlab, y, N, V, ignore_index, lse, bloss, bcnt, bbad);
+  launch(FLCE_KERNEL_FWD_FINALIZE, fwd_finalize, dim3(1), dim3(256), s, bloss, bcnt, bbad, L.nblk, loss, n_valid, dev_status);
   return launched();
 }
 
@@ -1839,7 +1798,7 @@ flce_status backward_impl(const T* H, const T* W, const int64_t* y, const float*
   const int ld_slab = (int)L.vc;
   const int n_td = (int)ceil_div(D, kTile);
   (void)hipGetLastError();
-  bwd_prep<<<dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, s>>>(lse, y, n_valid, grad, N, V, ignore_index,
+  launch(FLCE_KERNEL_BWD_PREP, bwd_prep, dim3((unsigned)ceil_div(N, 256)), dim3(256), s, lse, y, n_valid, grad, N, V, ignore_index,
                                                                   fixed_scale, e2, coef, lab, oscale);
   // Chunks of whole 256-row tiles, spread evenly: chunk i of n covers tiles
   // [i T / n, (i + 1) T / n) of the T tiles, never more than the workspace's chunk size.
@@ -1859,95 +1818,32 @@ flce_status backward_impl(const T* H, const T* W, const int64_t* y, const float*
       const int vc_act = (v1c < V ? v1c : V) - v0c;
       const int n_vt = (int)ceil_div(vc_act, kTile);
       if constexpr (sizeof(T) == 2)
-        bwd_dz16<T><<<dim3(grid(n_vt * n_tt)), dim3(kThreads), 0, s>>>(H, W, D, v0c, vc_act, t0c, tc_act, n_tt,
+        launch(FLCE_KERNEL_DZ, bwd_dz16<T>, dim3(grid(n_vt * n_tt)), dim3(kThreads), s, H, W, D, v0c, vc_act, t0c, tc_act, n_tt,
                                                                        e2, coef, lab, slab, ld_slab);
       else
-        bwd_dz<T><<<dim3(grid(n_vt * n_tt)), dim3(kThreads), 0, s>>>(H, W, D, v0c, vc_act, t0c, tc_act, n_tt, e2,
+        launch(FLCE_KERNEL_DZ, bwd_dz<T>, dim3(grid(n_vt * n_tt)), dim3(kThreads), s, H, W, D, v0c, vc_act, t0c, tc_act, n_tt, e2,
                                                                      coef, lab, slab, ld_slab);
       const dim3 gh(grid(n_tt * n_td)), gw(grid(n_vt * n_td)), blk(kThreads);
       const bool acc_dh = vi > 0, fin = dacc && vi == n_vc - 1;
       if (!acc_dh && !fin)
-        bwd_dh<T, false, false><<<gh, blk, 0, s>>>(slab, ld_slab, W, D, v0c, vc_act, t0c, tc_act, n_td, acc_rows, dH,
+        launch(FLCE_KERNEL_DH, bwd_dh<T, false, false>, gh, blk, s, slab, ld_slab, W, D, v0c, vc_act, t0c, tc_act, n_td, acc_rows, dH,
                                                 oscale);
       else if (acc_dh && !fin)
-        bwd_dh<T, true, false><<<gh, blk, 0, s>>>(slab, ld_slab, W, D, v0c, vc_act, t0c, tc_act, n_td, acc_rows, dH,
+        launch(FLCE_KERNEL_DH_ACC, bwd_dh<T, true, false>, gh, blk, s, slab, ld_slab, W, D, v0c, vc_act, t0c, tc_act, n_td, acc_rows, dH,
                                                 oscale);
       else if (!acc_dh && fin)
-        bwd_dh<T, false, true><<<gh, blk, 0, s>>>(slab, ld_slab, W, D, v0c, vc_act, t0c, tc_act, n_td, acc_rows, dH,
+        launch(FLCE_KERNEL_DH_FINAL, bwd_dh<T, false, true>, gh, blk, s, slab, ld_slab, W, D, v0c, vc_act, t0c, tc_act, n_td, acc_rows, dH,
                                                 oscale);
       else
-        bwd_dh<T, true, true><<<gh, blk, 0, s>>>(slab, ld_slab, W, D, v0c, vc_act, t0c, tc_act, n_td, acc_rows, dH,
+        launch(FLCE_KERNEL_DH_ACC_FINAL, bwd_dh<T, true, true>, gh, blk, s, slab, ld_slab, W, D, v0c, vc_act, t0c, tc_act, n_td, acc_rows, dH,
                                                 oscale);
       if (ci > 0)
-        bwd_dw<T, true><<<gw, blk, 0, s>>>(slab, ld_slab, H, D, t0c, tc_act, v0c, vc_act, n_td, dW, oscale);
+        launch(FLCE_KERNEL_DW_ACC, bwd_dw<T, true>, gw, blk, s, slab, ld_slab, H, D, t0c, tc_act, v0c, vc_act, n_td, dW, oscale);
       else
-        bwd_dw<T, false><<<gw, blk, 0, s>>>(slab, ld_slab, H, D, t0c, tc_act, v0c, vc_act, n_td, dW, oscale);
+        launch(FLCE_KERNEL_DW, bwd_dw<T, false>, gw, blk, s, slab, ld_slab, H, D, t0c, tc_act, v0c, vc_act, n_td, dW, oscale);
     }
   }
   return launched();
-}
-
-// Single-pass workspace for token chunks of tc rows (a multiple of 256): each chunk keeps
-// its exponentials for the whole vocabulary, keep [tc][ld] in the input type (ld = V
-// rounded up to 256) and mkeep [tc][ld / 128] fp32; plus the forward partials of one chunk,
-// per-row terms of one chunk, and block sums over all N rows.
-struct SpLayout {
-  int64_t tc, ld, ld_m;
-  int splits, nblk;
-  size_t lcnt, lbad, nv, part, zlab, bloss, bcnt, bbad, e2, coef, lab, oscale, mkeep, keep, total;
-};
-
-SpLayout sp_layout(int64_t N, int64_t V, int dtype, int64_t tc) {
-  SpLayout L;
-  L.tc = tc;
-  L.ld = round_up(V, kTile);
-  L.ld_m = L.ld / 128;
-  const int64_t ntn = L.tc / kTile, n_vt = L.ld / kTile;
-  int64_t sp = kPersistentWGs / ntn;
-  L.splits = (int)(sp < 1 ? 1 : (sp > n_vt ? n_vt : sp));
-  L.nblk = (int)ceil_div(N, 256);
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    const size_t o = off;
-    off += region(bytes);
-    return o;
-  };
-  L.lcnt = take((size_t)L.nblk * 4);
-  L.lbad = take((size_t)L.nblk * 4);
-  L.nv = take(4);
-  // part[split][row] of one chunk: splits x token tiles <= kPersistentWGs, so at most
-  // kPersistentWGs x 256 partials for any chunk (a short last chunk has more splits).
-  L.part = take((size_t)kPersistentWGs * kTile * sizeof(float2));
-  L.zlab = take((size_t)L.tc * 4);
-  L.bloss = take((size_t)L.nblk * 8);
-  L.bcnt = take((size_t)L.nblk * 4);
-  L.bbad = take((size_t)L.nblk * 4);
-  L.e2 = take((size_t)L.tc * 4);
-  L.coef = take((size_t)L.tc * 4);
-  L.lab = take((size_t)L.tc * 4);
-  L.oscale = take(4);
-  L.mkeep = take((size_t)L.tc * (size_t)L.ld_m * 4);
-  L.keep = take((size_t)L.tc * (size_t)L.ld * elem_size(dtype));
-  L.total = off;
-  return L;
-}
-
-// The smallest single-pass chunk: min(N, 4096) rows rounded up to 256.
-int64_t sp_min_chunk(int64_t N) { return round_up(N < kDefaultTokenChunk ? N : kDefaultTokenChunk, kTile); }
-
-// The largest chunk whose single-pass layout fits `ws`: the smallest chunk, then multiples
-// of 4096 rows up to N (a chunk of all N rows needs no read-modify-write of dW).  False if
-// even the smallest does not fit.
-bool sp_pick(int64_t N, int64_t V, int dtype, size_t ws, SpLayout* out) {
-  int64_t best = sp_min_chunk(N);
-  if (sp_layout(N, V, dtype, best).total > ws) return false;
-  for (int64_t tc = 2 * kDefaultTokenChunk; tc - kDefaultTokenChunk < N; tc += kDefaultTokenChunk) {
-    const int64_t t = round_up(tc < N ? tc : N, kTile);
-    if (sp_layout(N, V, dtype, t).total > ws) break;
-    best = t;
-  }
-  *out = sp_layout(N, V, dtype, best);
-  return true;
 }
 
 // Forward and backward without recomputing logits: per token chunk, the logit GEMM keeps
@@ -1978,45 +1874,44 @@ flce_status single_pass_impl(const T* H, const T* W, const int64_t* y, const flo
   const int n_chunks = (int)ceil_div(N, L.tc);
   auto grid = [](int64_t tiles) { return (unsigned)(tiles < kPersistentWGs ? tiles : kPersistentWGs); };
   (void)hipGetLastError();
-  label_blocks<<<dim3((unsigned)L.nblk), dim3(256), 0, s>>>(y, N, V, ignore_index, lcnt, lbad);
-  label_total<<<dim3(1), dim3(256), 0, s>>>(lcnt, L.nblk, nv);
+  launch(FLCE_KERNEL_LABELS, label_blocks, dim3((unsigned)L.nblk), dim3(256), s, y, N, V, ignore_index, lcnt, lbad);
+  launch(FLCE_KERNEL_LABELS, label_total, dim3(1), dim3(256), s, lcnt, L.nblk, nv);
   for (int ci = 0; ci < n_chunks; ++ci) {
     const int t0 = (int)(ci * L.tc);
     const int rows = (int)(N - t0 < L.tc ? N - t0 : L.tc);
     const int ntn = (int)ceil_div(rows, kTile);
-    const int splits = (int)(kPersistentWGs / ntn < 1 ? 1 : (kPersistentWGs / ntn > L.ld / kTile ? L.ld / kTile
-                                                                                                 : kPersistentWGs / ntn));
+    const int splits = (int)flce_plan::fwd_splits(rows, V);
     if constexpr (sizeof(T) == 2)
-      fwd_tiles16<T, true><<<dim3((unsigned)(ntn * splits)), dim3(kThreads), 0, s>>>(
+      launch(FLCE_KERNEL_FWD_KEEP, fwd_tiles16<T, true>, dim3((unsigned)(ntn * splits)), dim3(kThreads), s,
           H + (int64_t)t0 * D, W, y + t0, rows, D, V, ntn, splits, part, zlab, keep, ld, mkeep, ld_m);
     else
-      fwd_tiles<T, true><<<dim3((unsigned)(ntn * splits)), dim3(kThreads), 0, s>>>(
+      launch(FLCE_KERNEL_FWD_KEEP, fwd_tiles<T, true>, dim3((unsigned)(ntn * splits)), dim3(kThreads), s,
           H + (int64_t)t0 * D, W, y + t0, rows, D, V, ntn, splits, part, zlab, keep, ld, mkeep, ld_m);
     const int blk0 = t0 / 256;
-    fwd_combine<<<dim3((unsigned)ceil_div(rows, 256)), dim3(256), 0, s>>>(part, splits, zlab, y + t0, rows, V,
+    launch(FLCE_KERNEL_FWD_COMBINE, fwd_combine, dim3((unsigned)ceil_div(rows, 256)), dim3(256), s, part, splits, zlab, y + t0, rows, V,
                                                                           ignore_index, lse + t0, bloss + blk0,
                                                                           bcnt + blk0, bbad + blk0);
-    bwd_prep<<<dim3((unsigned)ceil_div(rows, 256)), dim3(256), 0, s>>>(lse + t0, y + t0, nv, grad, rows, V,
+    launch(FLCE_KERNEL_BWD_PREP, bwd_prep, dim3((unsigned)ceil_div(rows, 256)), dim3(256), s, lse + t0, y + t0, nv, grad, rows, V,
                                                                        ignore_index, fixed_scale, e2, coef, lab, oscale);
     const int P = (int)ceil_div(ld / Pack16<T>::K, kDzThreads);
     const int64_t pieces = (int64_t)rows * P;
-    keep_to_dz<T><<<dim3((unsigned)(pieces < (1 << 20) ? pieces : (1 << 20))), dim3(kDzThreads), 0, s>>>(
+    launch(FLCE_KERNEL_KEEP_TO_DZ, keep_to_dz<T>, dim3((unsigned)(pieces < (1 << 20) ? pieces : (1 << 20))), dim3(kDzThreads), s,
         keep, ld, rows, mkeep, ld_m, e2, coef, lab, pieces, P);
     const int n_tt = ntn, n_vt = (int)ceil_div(V, kTile);
     if (dtype == FLCE_F32)
-      bwd_dh<T, false, false><<<dim3(grid((int64_t)n_tt * n_td)), dim3(kThreads), 0, s>>>(
+      launch(FLCE_KERNEL_DH, bwd_dh<T, false, false>, dim3(grid((int64_t)n_tt * n_td)), dim3(kThreads), s,
           keep, ld, W, D, 0, V, t0, rows, n_td, reinterpret_cast<float*>(dH) + (int64_t)t0 * D, dH, oscale);
     else
-      bwd_dh<T, false, true><<<dim3(grid((int64_t)n_tt * n_td)), dim3(kThreads), 0, s>>>(
+      launch(FLCE_KERNEL_DH_FINAL, bwd_dh<T, false, true>, dim3(grid((int64_t)n_tt * n_td)), dim3(kThreads), s,
           keep, ld, W, D, 0, V, t0, rows, n_td, reinterpret_cast<float*>(ws), dH, oscale);
     if (ci > 0)
-      bwd_dw<T, true><<<dim3(grid((int64_t)n_vt * n_td)), dim3(kThreads), 0, s>>>(keep, ld, H, D, t0, rows, 0, V,
+      launch(FLCE_KERNEL_DW_ACC, bwd_dw<T, true>, dim3(grid((int64_t)n_vt * n_td)), dim3(kThreads), s, keep, ld, H, D, t0, rows, 0, V,
                                                                                   n_td, dW, oscale);
     else
-      bwd_dw<T, false><<<dim3(grid((int64_t)n_vt * n_td)), dim3(kThreads), 0, s>>>(keep, ld, H, D, t0, rows, 0, V,
+      launch(FLCE_KERNEL_DW, bwd_dw<T, false>, dim3(grid((int64_t)n_vt * n_td)), dim3(kThreads), s, keep, ld, H, D, t0, rows, 0, V,
                                                                                    n_td, dW, oscale);
   }
-  fwd_finalize<<<dim3(1), dim3(256), 0, s>>>(bloss, bcnt, bbad, L.nblk, loss, n_valid, dev_status);
+  launch(FLCE_KERNEL_FWD_FINALIZE, fwd_finalize, dim3(1), dim3(256), s, bloss, bcnt, bbad, L.nblk, loss, n_valid, dev_status);
   return launched();
 }
 
@@ -2027,7 +1922,7 @@ extern "C" {
 size_t flce_workspace_bytes(int64_t N, int64_t D, int64_t V, int dtype) {
   if (!sizes_ok(N, D, V, dtype)) return 0;
   const size_t f = fwd_layout(N, V).total;
-  const size_t b = default_bwd_bytes(N, D, V, dtype);
+  const size_t b = flce_plan::default_bwd_bytes(N, D, V, dtype);
   return f > b ? f : b;
 }
 
@@ -2075,7 +1970,7 @@ flce_status flce_backward(const void* H, const void* W, const int64_t* y, const 
     return FLCE_ERR_ALIGN;
   int64_t tc = 0, vc = 0;
   if (!pick_chunks(N, D, V, dtype, workspace_bytes, &tc, &vc)) return FLCE_ERR_WORKSPACE;
-  const BwdLayout L = bwd_layout(N, D, dtype, tc, vc);
+  const BwdLayout L = flce_plan::bwd_layout(N, D, dtype, tc, vc);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = reinterpret_cast<char*>(workspace);
   if (dtype == FLCE_BF16)
@@ -2093,7 +1988,24 @@ flce_status flce_backward(const void* H, const void* W, const int64_t* y, const 
 
 size_t flce_forward_backward_workspace_bytes(int64_t N, int64_t D, int64_t V, int dtype) {
   if (!sizes_ok(N, D, V, dtype)) return 0;
-  return sp_layout(N, V, dtype, sp_min_chunk(N)).total;
+  const int64_t first = flce_plan::sp_min_chunk(N, D, V, dtype);
+  if (first < flce_plan::kTile) return flce_workspace_bytes(N, D, V, dtype);
+  return flce_plan::sp_layout(N, V, dtype, first).total;
+}
+
+flce_status flce_forward_backward_chunk(int64_t N, int64_t D, int64_t V, int dtype, size_t workspace_bytes,
+                                        int64_t* token_chunk) {
+  if (!sizes_ok(N, D, V, dtype)) return FLCE_ERR_INVALID_ARG;
+  SpLayout L;
+  int64_t tc = 0, vc = 0;
+  if (flce_plan::sp_pick(N, D, V, dtype, workspace_bytes, &L))
+    tc = L.tc;
+  else if (workspace_bytes < fwd_layout(N, V).total || !pick_chunks(N, D, V, dtype, workspace_bytes, &tc, &vc))
+    return FLCE_ERR_WORKSPACE;
+  else
+    tc = 0;
+  if (token_chunk) *token_chunk = tc;
+  return FLCE_OK;
 }
 
 flce_status flce_forward_backward(const void* H, const void* W, const int64_t* y, int64_t N, int64_t D, int64_t V,
@@ -2111,7 +2023,7 @@ flce_status flce_forward_backward(const void* H, const void* W, const int64_t* y
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = reinterpret_cast<char*>(workspace);
   SpLayout L;
-  if (sp_pick(N, V, dtype, workspace_bytes, &L)) {
+  if (flce_plan::sp_pick(N, D, V, dtype, workspace_bytes, &L)) {
     if (dtype == FLCE_BF16)
       return single_pass_impl<u16>(reinterpret_cast<const u16*>(H), reinterpret_cast<const u16*>(W), y, grad_loss,
                                    (int)N, (int)D, (int)V, dtype, ignore_index, loss, lse, n_valid, dev_status,
@@ -2135,6 +2047,21 @@ flce_status flce_forward_backward(const void* H, const void* W, const int64_t* y
   if (f != FLCE_OK) return f;
   return flce_backward(H, W, y, lse, n_valid, grad_loss, N, D, V, dtype, ignore_index, dH, dW, workspace,
                        workspace_bytes, stream);
+}
+
+int32_t flce_timing_begin(void** events, int32_t* kernel_ids, int32_t capacity) {
+  if (!events || !kernel_ids || capacity < 1) return FLCE_ERR_INVALID_ARG;
+  g_timing.events = reinterpret_cast<hipEvent_t*>(events);
+  g_timing.ids = kernel_ids;
+  g_timing.capacity = capacity;
+  g_timing.count = 0;
+  return FLCE_OK;
+}
+
+int32_t flce_timing_end(void) {
+  const int32_t n = g_timing.count;
+  g_timing = LaunchTiming{};
+  return n;
 }
 
 const char* flce_status_string(int status) {

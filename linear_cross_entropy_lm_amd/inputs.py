@@ -98,6 +98,14 @@ def case(N: int, D: int, V: int, dtype: str = "bf16", seed: int = 7, **kw) -> Co
                   seed=seed, **base)
 
 
+# Test-only workloads with stored oracle values (tests/golden/fullsize_<name>.npz).
+GOLDEN_CASES = {
+    # 16640 rows at the Qwen-2.5 vocabulary: one single-pass chunk of every row would span
+    # 16640 x 152064 x 2 bytes, past 32-bit offsets, so the single pass runs capped chunks
+    "spcap_bf16": case(16640, 64, 152064, "bf16", seed=1010),
+}
+
+
 # ---------------------------------------------------------------------------------
 # bf16 bit-pattern helpers (format conversion only)
 # ---------------------------------------------------------------------------------
@@ -507,6 +515,14 @@ class NormInputs:
             t = t if self.cfg.dtype == "f32" else t.view(self.torch_dtype)
             return t.to(device).contiguous()
         return dev(self.X), dev(self.gamma), dev(self.dH)
+
+    def digest(self) -> str:
+        """Fingerprint of the exact input bytes (xxh3-128 over X, gamma, dH)."""
+        import xxhash
+        h = xxhash.xxh3_128()
+        for t in (self.X, self.gamma, self.dH):
+            h.update(memoryview(t.contiguous().numpy()).cast("B"))
+        return h.hexdigest()
 
 
 def generate_norm(cfg: NormConfig, threads: int = 8) -> NormInputs:

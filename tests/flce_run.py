@@ -72,3 +72,38 @@ def compare(got: dict, ref: dict, dtype: str, grads: bool = True) -> dict:
                 err[k] = rel_fro(got[k], ref[k])
                 assert err[k] <= tol["grad"], err
     return err
+
+
+def gather_windows(t, rows, cols, width):
+    """t[rows[i], cols[i] : cols[i] + width] for every i (device tensor in, fp64 numpy out)."""
+    idx_r = torch.as_tensor(rows, device=t.device).repeat_interleave(width)
+    idx_c = (torch.as_tensor(cols, device=t.device)[:, None]
+             + torch.arange(width, device=t.device)[None, :]).reshape(-1)
+    return t[idx_r, idx_c].reshape(len(rows), width).double().cpu().numpy()
+
+
+def compare_golden(gold, loss, lse, dH, dW, dtype: str) -> dict:
+    """A full-size GPU result (device tensors; dH, dW already divided by any loss scale)
+    against stored oracle values: the loss, every row's lse, whole sampled rows of dH and dW,
+    and the first and last row of every 256-row token tile (dH) and vocabulary tile (dW) over
+    a walking 256-column window.  Asserts the dtype's tolerances; returns the errors."""
+    tol = TOL[dtype]
+    D = dH.shape[1]
+    width = min(256, D)
+    err = {
+        "loss": abs(float(loss.item()) - float(gold["loss"])) / float(gold["loss"]),
+        "lse": float(np.max(np.abs(lse.cpu().double().numpy() - gold["lse"]) / np.abs(gold["lse"]))),
+        "dH_rows": rel_fro(dH[torch.as_tensor(gold["dh_rows"], device=dH.device)].double().cpu().numpy(),
+                           gold["dh"]),
+        "dW_rows": rel_fro(dW[torch.as_tensor(gold["dw_rows"], device=dW.device)].double().cpu().numpy(),
+                           gold["dw"]),
+        "dH_tile_edges": rel_fro(gather_windows(dH, gold["dh_edge_rows"], gold["dh_edge_cols"], width),
+                                 gold["dh_edge"]),
+        "dW_tile_edges": rel_fro(gather_windows(dW, gold["dw_edge_rows"], gold["dw_edge_cols"], width),
+                                 gold["dw_edge"]),
+    }
+    assert err["loss"] <= tol["loss"], err
+    assert err["lse"] <= tol["lse"], err
+    for k in ("dH_rows", "dW_rows", "dH_tile_edges", "dW_tile_edges"):
+        assert err[k] <= tol["grad"], err
+    return err

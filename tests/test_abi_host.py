@@ -223,13 +223,51 @@ def test_single_pass_workspace_formula(B):
         T = min(-(-N // 256) * 256, 4096)
         ld = -(-V // 256) * 256
         nblk = -(-N // 256)
-        expect = (2 * _r(nblk * 4) + _r(4) + _r(256 * 256 * 8) + _r(T * 4) + _r(nblk * 8) + 2 * _r(nblk * 4)
+        expect = (2 * _r(nblk * 4) + _r(4) + _r(max(256 * 256, T) * 8) + _r(T * 4) + _r(nblk * 8) + 2 * _r(nblk * 4)
                   + 3 * _r(T * 4) + _r(4) + _r(T * (ld // 128) * 4) + _r(T * ld * es))
         assert B.flce_forward_backward_workspace_bytes(N, D, V, dt) == expect
     # 25% of the 16-bit logit bytes at the Llama-3 shape: the price of skipping the recompute
     frac = B.flce_forward_backward_workspace_bytes(16384, 4096, 128256, 1) / (16384 * 128256 * 2)
     assert 0.25 < frac < 0.26
     assert B.flce_forward_backward_workspace_bytes(0, 64, 64, 1) == 0
+
+
+def test_single_pass_chunk_choice(B):
+    """The token chunk flce_forward_backward takes: the least workspace buys min(N, 4096)
+    rows, more buys multiples of 4096 up to N, within the 32-bit offset cap; below the
+    least the call takes the two-call schedule (chunk 0)."""
+    N, D, V = 16384, 4096, 128256
+    least = B.flce_forward_backward_workspace_bytes(N, D, V, 1)
+    assert B.flce_forward_backward_chunk(N, D, V, 1, least) == 4096
+    assert B.flce_forward_backward_chunk(N, D, V, 1, 2 * least) == 8192
+    # 12288 rows of the kept slab would span 3.2e9 bytes, past the 2^31 offset limit
+    assert B.flce_forward_backward_chunk(N, D, V, 1, 10 * least) == 8192
+    assert B.flce_forward_backward_chunk(N, D, V, 1, least - 1) == 0
+    assert B.flce_forward_backward_chunk(N, D, V, 1, B.flce_workspace_bytes(N, D, V, 1)) == 0
+    with pytest.raises(B.FlceError) as e:
+        B.flce_forward_backward_chunk(N, D, V, 1, 4096)
+    assert e.value.code == B.FLCE_ERR_WORKSPACE
+    # the case that wrapped 32-bit offsets (16640 x 304128 bytes = 5.06e9) is capped
+    assert B.flce_forward_backward_chunk(16640, 64, 152064, 1, 6 * 10**9) == 4096
+    # fp32 at a 152064-row vocabulary: 3328 rows is the widest chunk within the limit
+    assert B.flce_forward_backward_chunk(8192, 1024, 152064, 0, 10**12) == 3328
+
+
+def test_single_pass_unavailable_falls_back(B):
+    """Where W is too large for one dH contraction (V D es > 2^31), the single pass does not
+    run: the workspace query returns the two-call schedule's need and the call takes it."""
+    for N, D, V, dt in [(8192, 4096, 152064, 0), (8192, 8192, 152064, 1)]:
+        two = B.flce_workspace_bytes(N, D, V, dt)
+        assert B.flce_forward_backward_workspace_bytes(N, D, V, dt) == two
+        assert B.flce_forward_backward_chunk(N, D, V, dt, two) == 0
+        assert B.flce_forward_backward_chunk(N, D, V, dt, 10**12) == 0
+
+
+def test_widest_fp32_rows_trim_the_vocab_chunk(B):
+    """At D = 65536 fp32 an 8192-row vocabulary chunk of W spans exactly 2^31 bytes: the
+    default chunk drops to 7936."""
+    ws = B.flce_workspace_bytes(16384, 65536, 128256, 0)
+    assert B.flce_backward_chunks(16384, 65536, 128256, 0, ws) == (4096, 7936)
 
 
 # Every call below has an argument the library rejects before launching anything.
@@ -251,3 +289,4 @@ def test_forward_backward_argument_errors(B):
     # enough for the forward but not the backward: rejected before the forward launches
     fwd_only = B.flce_workspace_bytes(512, 64, 1024, 1) // 16
     assert _fb(B, wsb=fwd_only) == B.FLCE_ERR_WORKSPACE
+

@@ -126,3 +126,50 @@ def test_norm_lm_head_cross_entropy_chain(dtype):
     e_dw = rel_fro(Wr.grad.double().cpu().numpy(), ref["dW"])
     _say("chain errors", dict(loss=e_loss, dX=e_dx, dgamma=e_dg, dW=e_dw))
     assert e_loss <= tol and e_dx <= tol and e_dg <= tol and e_dw <= tol
+
+
+def test_norm_lm_head_cross_entropy_chain_fullsize():
+    """The chain at full size: the final norm of norm_llama3 (16384 x 4096 bf16) feeding the
+    Llama-3-shaped head (V = 128256) through NormLinearCrossEntropy, against the stored
+    oracle run (H and dH stored in bf16 at the points the kernels hand them on): the loss,
+    dX at whole sampled rows and at the first and last row of every 256-row tile over a
+    walking 256-column window, dgamma on every channel, and dW rows at every vocabulary tile
+    edge.  The wrapper returns dgamma and dW cast to the weights' bf16 (one more rounding,
+    2^-9)."""
+    import os
+    from linear_cross_entropy_lm_amd import binding as B
+    from flce_run import gather_windows
+    gold = np.load(os.path.join(os.path.dirname(__file__), "golden", "fullsize_chain_llama3.npz"))
+    ncfg, hcfg = I.NORM_CONFIGS["norm_llama3"], I.CONFIGS["llama3"]
+    _say("case", ncfg.describe(), "->", hcfg.describe())
+    ninp, hinp = I.generate_norm(ncfg), I.generate(hcfg)
+    assert ninp.digest() + hinp.digest() == str(gold["digest"]), "seeded inputs differ from the stored oracle run"
+    dev = "cuda:0"
+    X, g, _ = ninp.device_tensors(dev)
+    _, W, y = hinp.device_tensors(dev)
+    Xr = X.clone().requires_grad_(True)
+    gr = g.clone().requires_grad_(True)
+    Wr = W.clone().requires_grad_(True)
+    del X, W
+    loss = B.NormLinearCrossEntropy.apply(Xr, gr, Wr, y, ncfg.eps)
+    loss.backward()
+    torch.cuda.synchronize()
+    width = 256
+    err = {
+        "loss": abs(loss.item() - float(gold["loss"])) / float(gold["loss"]),
+        "dX_rows": rel_fro(Xr.grad[torch.as_tensor(gold["dx_rows"], device=dev)].double().cpu().numpy(),
+                           gold["dx"]),
+        "dX_tile_edges": rel_fro(gather_windows(Xr.grad, gold["dx_edge_rows"], gold["dx_edge_cols"], width),
+                                 gold["dx_edge"]),
+        "dgamma": rel_fro(gr.grad.double().cpu().numpy(), gold["dgamma"]),
+        "dW_rows": rel_fro(Wr.grad[torch.as_tensor(gold["dw_rows"], device=dev)].double().cpu().numpy(),
+                           gold["dw"]),
+        "dW_tile_edges": rel_fro(gather_windows(Wr.grad, gold["dw_edge_rows"], gold["dw_edge_cols"], width),
+                                 gold["dw_edge"]),
+    }
+    _say("chain errors", err)
+    assert err["loss"] <= 2e-3
+    for k in ("dX_rows", "dX_tile_edges", "dgamma", "dW_rows", "dW_tile_edges"):
+        assert err[k] <= 1e-2, err
+    del Xr, gr, Wr, loss
+    torch.cuda.empty_cache()

@@ -137,7 +137,7 @@ def test_large_logits_stable(dtype):
     got = run_gpu(inp)
     ref = _oracle(inp)
     assert np.max(np.abs(ref["lse"])) > 100
-    compare(got, ref, "bf16")
+    _say("errors", compare(got, ref, dtype))
 
 
 def test_invalid_label_sets_status_and_is_ignored():
@@ -208,8 +208,30 @@ def test_autograd_wrapper():
     (3.0 * loss).backward()
     ref = _oracle(inp, g=3.0)
     assert abs(loss.item() - ref["loss"]) <= 2e-3 * ref["loss"]
-    assert rel_fro(H.grad.float().cpu().double().numpy(), ref["dH"]) <= 1e-2
-    assert rel_fro(W.grad.float().cpu().double().numpy(), ref["dW"]) <= 1.5e-2
+    e_dh = rel_fro(H.grad.float().cpu().double().numpy(), ref["dH"])
+    e_dw = rel_fro(W.grad.float().cpu().double().numpy(), ref["dW"])
+    _say("autograd errors", dict(dH=e_dh, dW=e_dw))
+    # W.grad is the fp32 dW rounded to bf16 (the weights' dtype): within the same 1e-2
+    assert e_dh <= 1e-2 and e_dw <= 1e-2
+
+
+def test_autograd_wrapper_rejects_bad_labels():
+    """The torch wrapper reads the forward's device status: a label outside [0, V) that is
+    not ignore_index raises (the oracle's convention); with check_labels=False the row is
+    treated as ignored, as the C ABI documents."""
+    from linear_cross_entropy_lm_amd import binding as B
+    cfg = I.case(300, 256, 1000, "bf16", seed=51, ignore_frac=0.0)
+    inp0 = I.generate(cfg)
+    y = inp0.y.clone()
+    y[9] = 1000
+    H, W, yd = I.with_labels(inp0, y).device_tensors("cuda:0")
+    with pytest.raises(ValueError):
+        B.fused_linear_cross_entropy(H, W, yd)
+    loss = B.fused_linear_cross_entropy(H, W, yd, check_labels=False)
+    y_ref = y.clone()
+    y_ref[9] = -100
+    ref = _oracle(I.with_labels(inp0, y_ref))
+    assert abs(loss.item() - ref["loss"]) <= 2e-3 * ref["loss"]
 
 
 def test_library_allocates_no_device_memory():
