@@ -26,9 +26,9 @@ def test_norm_bytes():
     assert bench.norm_bytes(3, 8, 4, 3)[1] == 3 * 3 * 8 * 4 + 12 + 32 + 2 * 3 * 8 * 4 + 2 * 1 * 8 * 4 + 32
 
 
-def _write_counters(path, kernel, counter, values):
+def _write_counters(path, kernel, counter, values, tag="x"):
     os.makedirs(path, exist_ok=True)
-    with open(os.path.join(path, "x_counter_collection.csv"), "w", newline="") as f:
+    with open(os.path.join(path, f"{tag}_counter_collection.csv"), "w", newline="") as f:
         w = csv.writer(f)
         w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
         for i, v in enumerate(values):
@@ -38,32 +38,75 @@ def _write_counters(path, kernel, counter, values):
         w.writerow([99, "other_kernel", counter, 1e9])
 
 
-@pytest.mark.parametrize("path", sorted(bench.PATHS))
-def test_summarize_counters_scales_by_the_copy(tmp_path, monkeypatch, path):
-    kernel = bench.PATHS[path][0]
-    rec_file = tmp_path / "rec.json"
-    monkeypatch.setitem(bench.PATHS, path, (kernel, "w", str(rec_file), bench.PATHS[path][3]))
+@pytest.mark.parametrize("path,kinds", [("fused", ["fwd_tiles16", "bwd_dz16", "bwd_dh", "bwd_dw"]),
+                                        ("single", ["fwd_tiles16_keep", "bwd_dw"]), ("ce", ["ce_rows_bwd"]),
+                                        ("norm", ["rms_bwd"])])
+def test_summarize_counters_scales_by_the_copy(tmp_path, monkeypatch, path, kinds):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
     root = tmp_path / "cnt"
     copy = 1 << 30
-    _write_counters(root / "F", kernel, "FETCH_SIZE", [1000.0, 3000.0])
-    _write_counters(root / "W", kernel, "WRITE_SIZE", [500.0, 500.0])
+    names = {"fwd_tiles16": "(anonymous namespace)::fwd_tiles16<unsigned short, false>",
+             "fwd_tiles16_keep": "(anonymous namespace)::fwd_tiles16<unsigned short, true>",
+             "bwd_dz16": "(anonymous namespace)::bwd_dz16<unsigned short>",
+             "bwd_dh": "(anonymous namespace)::bwd_dh<unsigned short, true, false>",
+             "bwd_dw": "(anonymous namespace)::bwd_dw<unsigned short, true>",
+             "ce_rows_bwd": "(anonymous namespace)::ce_rows_bwd<1>", "rms_bwd": "(anonymous namespace)::rms_bwd<1, 2>"}
+    for i, kind in enumerate(kinds):
+        _write_counters(root / "F", names[kind], "FETCH_SIZE", [1000.0 * (i + 1), 3000.0 * (i + 1)], f"k{i}")
+        _write_counters(root / "W", names[kind], "WRITE_SIZE", [500.0, 500.0], f"k{i}")
     # a 1 GiB copy whose counters read half the fetched bytes and all the written bytes
     _write_counters(root / "FC", "__amd_rocclr_copyBuffer", "FETCH_SIZE", [copy / 2048.0])
     _write_counters(root / "WC", "__amd_rocclr_copyBuffer", "WRITE_SIZE", [copy / 1024.0])
-    rec = bench.summarize_counters(str(root), copy, path)
-    assert rec["fetch_kib_per_launch"] == 2000.0 and rec["write_kib_per_launch"] == 500.0
-    assert rec["fetch_factor"] == pytest.approx(2.0) and rec["write_factor"] == pytest.approx(1.0)
-    assert rec["hbm_bytes_per_launch"] == pytest.approx(2000.0 * 1024 * 2 + 500.0 * 1024)
-    assert json.loads(rec_file.read_text())["source_digest"] == bench.source_digest(path)
-    assert bench.load_traffic(path) == pytest.approx(rec["hbm_bytes_per_launch"])
+    recs = bench.summarize_counters(str(root), copy, path, kinds, "w")
+    for i, (kind, rec) in enumerate(zip(kinds, recs)):
+        assert rec["fetch_kib_per_launch"] == 2000.0 * (i + 1) and rec["write_kib_per_launch"] == 500.0
+        assert rec["fetch_factor"] == pytest.approx(2.0) and rec["write_factor"] == pytest.approx(1.0)
+        assert rec["hbm_bytes_per_launch"] == pytest.approx(2000.0 * (i + 1) * 1024 * 2 + 500.0 * 1024)
+        saved = json.loads(open(bench.traffic_path(kind, "w")).read())
+        assert saved["source_digest"] == bench.source_digest(path)
+        assert bench.load_traffic(kind, "w", path) == pytest.approx(rec["hbm_bytes_per_launch"])
+
+
+def test_kernel_patterns_tell_the_forward_variants_apart():
+    import re
+    plain = "void (anonymous namespace)::fwd_tiles16<(anonymous namespace)::h16, false>(int)"
+    keep = "void (anonymous namespace)::fwd_tiles16<unsigned short, true>(int)"
+    assert re.search(bench.KINDS["fwd_tiles16"][0], plain) and not re.search(bench.KINDS["fwd_tiles16"][0], keep)
+    assert re.search(bench.KINDS["fwd_tiles16_keep"][0], keep)
+    assert not re.search(bench.KINDS["fwd_tiles16_keep"][0], plain)
 
 
 def test_traffic_record_of_another_source_is_ignored(tmp_path, monkeypatch):
-    rec_file = tmp_path / "rec.json"
-    rec_file.write_text(json.dumps({"source_digest": "0" * 16, "hbm_bytes_per_launch": 1.0}))
-    kernel, wl, _, src = bench.PATHS["fused"]
-    monkeypatch.setitem(bench.PATHS, "fused", (kernel, wl, str(rec_file), src))
-    assert bench.load_traffic("fused") is None
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    with open(bench.traffic_path("bwd_dw", "llama3"), "w") as f:
+        f.write(json.dumps({"source_digest": "0" * 16, "workload": "llama3", "hbm_bytes_per_launch": 1.0}))
+    assert bench.load_traffic("bwd_dw", "llama3") is None
+
+
+def test_chunk_spans_partition_whole_tiles():
+    for total, chunk in [(16384, 4096), (128256, 8192), (4097, 4096), (300, 4096), (152064, 8192)]:
+        spans = bench.chunk_spans(total, chunk)
+        assert spans[0][0] == 0 and sum(r for _, r in spans) == total
+        for (a, r), (b, _) in zip(spans, spans[1:]):
+            assert a + r == b and a % 256 == 0 and r % 256 == 0 and r <= chunk
+        assert spans[-1][1] <= chunk
+    assert bench.chunk_spans(128256, 8192)[0] == (0, 7936)  # 501 tiles over 16 chunks: 31 or 32 tiles
+
+
+@pytest.mark.parametrize("path,tc,vc", [("fused", 4096, 8192), ("single", 4096, 0), ("single", 8192, 0)])
+def test_gemm_launch_flops_cover_each_kind_once(path, tc, vc):
+    """Every GEMM kind's launches add up to one full 2 N V D contraction per step."""
+    N, D, V = 16384, 4096, 128256
+    launches = bench.gemm_launch_flops(path, N, D, V, tc, vc)
+    family = bench.GEMM_KINDS[path]["f16"]
+    for kind in family:
+        ids = set(bench.KINDS[kind][1])
+        assert sum(f for k, f in launches if k in ids) == pytest.approx(2.0 * N * V * D)
+    if path == "fused":
+        assert len(launches) == 1 + 3 * 4 * 16
+        assert [k for k, _ in launches[1:4]] == [5, 6, 10] and [k for k, _ in launches[-3:]] == [5, 9, 11]
+    else:
+        assert len(launches) == 3 * (N // tc)
 
 
 def test_more_than_one_gpu_is_refused(capsys, monkeypatch):
@@ -131,11 +174,9 @@ def test_sclk_sampler_reads_the_current_level(tmp_path):
 
 def test_traffic_record_of_another_workload_is_ignored(tmp_path, monkeypatch):
     """A record taken on the Llama-3 workload does not describe a run on another one."""
-    rec_file = tmp_path / "rec.json"
-    rec_file.write_text(json.dumps({"source_digest": bench.source_digest("fused"), "workload": "llama3",
-                                    "hbm_bytes_per_launch": 5.0}))
-    kernel, wl, _, src = bench.PATHS["fused"]
-    monkeypatch.setitem(bench.PATHS, "fused", (kernel, wl, str(rec_file), src))
-    assert bench.load_traffic("fused") == 5.0
-    assert bench.load_traffic("fused", "llama3") == 5.0
-    assert bench.load_traffic("fused", "llama2") is None
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    with open(bench.traffic_path("bwd_dh", "llama3"), "w") as f:
+        f.write(json.dumps({"source_digest": bench.source_digest("fused"), "workload": "llama3",
+                            "hbm_bytes_per_launch": 5.0}))
+    assert bench.load_traffic("bwd_dh", "llama3") == 5.0
+    assert bench.load_traffic("bwd_dh", "llama2") is None

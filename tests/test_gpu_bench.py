@@ -39,6 +39,15 @@ def test_bench_line(monkeypatch, capsys, argv):
     assert r["bound"] in ("mfma", "hbm") and r["achieved"] > 0 and 0 < r["frac"] < 1
     if "llama2" in argv:
         assert r["traffic"] is None  # the committed counter records describe other workloads
+    if "--path" not in argv or "single" in argv:
+        # per-kernel timing: the roofline names the GEMM kind with the largest time per step
+        ks = d["kernels"]
+        assert r["kernel"] == max(ks, key=lambda k: ks[k]["ms_per_step"])
+        for k in ks.values():
+            assert k["launches_per_step"] >= 1 and k["mean_us"] > 0 and 0 < k["frac"] < 1
+        assert sum(k["ms_per_step"] for k in ks.values()) < d["kernel_timing_step_ms"]
+        print("kernels", json.dumps(ks), "timed-launch step", d["kernel_timing_step_ms"], "plain step",
+              d["ms_per_step"], flush=True)
     cb = d["cpu_baseline"]
     if "--no-cpu-baseline" in argv:
         assert cb is None
