@@ -195,10 +195,41 @@ flce_status flce_forward_backward(const void* H, const void* W, const int64_t* y
                                   void* dH, float* dW, void* workspace, size_t workspace_bytes,
                                   void* stream);
 
+/* Bytes of the device array flce_forward_backward_static works in (one array per GPU). */
+#define FLCE_STATIC_SCRATCH_BYTES ((size_t)144 << 20)
+
+/*
+ * flce_forward_backward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * computation, arguments (minus the workspace) and outputs as flce_forward_backward, with
+ * the workspace taken from a fixed device array of FLCE_STATIC_SCRATCH_BYTES (144 MiB)
+ * inside the library: the schedule and results are those of flce_forward_backward with a
+ * caller workspace of that size (the recomputing schedule at the workload shapes here:
+ * 134.4 MB at N = 16384, D = 4096, V = 128256, bf16; the single pass where it fits).
+ *
+ * The call allocates and frees nothing.  Each GPU holds its own copy of the array until
+ * the process ends; its address is looked up once per device, on that device's first
+ * call (the first call may therefore make the runtime load the library's code object).
+ * Every call on one GPU shares that GPU's array, so calls that overlap on one GPU -- on
+ * different streams, or from different host threads without ordering -- race and give
+ * wrong results; calls ordered on one stream are safe.  Nothing in the array needs to
+ * start at zero: every call writes each byte it reads first.
+ *
+ * Errors: FLCE_ERR_WORKSPACE when the problem needs more scratch than the array holds
+ * (neither schedule fits FLCE_STATIC_SCRATCH_BYTES: the recomputing schedule needs 12
+ * bytes per row of N besides its chunks, so e.g. 16M rows at a vocabulary too wide for the
+ * single pass), reported before anything touches the device; FLCE_ERR_HIP when the array's
+ * address cannot be obtained or a launch fails; otherwise as flce_forward_backward.
+ */
+flce_status flce_forward_backward_static(const void* H, const void* W, const int64_t* y, int64_t N, int64_t D,
+                                         int64_t V, int dtype, int64_t ignore_index, const float* grad_loss,
+                                         float* loss, float* lse, int32_t* n_valid, int32_t* dev_status, void* dH,
+                                         float* dW, void* stream);
+
 /*
  * Launch timing, a measurement aid for benchmarks and profilers (the computation needs none
- * of it).  Every kernel launch of flce_forward, flce_backward and flce_forward_backward has one
- * of these ids:
+ * of it).  Every kernel launch of flce_forward, flce_backward, flce_forward_backward and
+ * flce_forward_backward_static has one of these ids:
  */
 enum flce_kernel_id {
   FLCE_KERNEL_FWD = 0,           /* forward logit tiles with the online log-sum-exp */

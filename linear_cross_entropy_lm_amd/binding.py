@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflce.so"
 
 FLCE_OK, FLCE_ERR_INVALID_ARG, FLCE_ERR_ALIGN, FLCE_ERR_WORKSPACE, FLCE_ERR_HIP = range(5)
 FLCE_F32, FLCE_BF16, FLCE_F16 = 0, 1, 2
+FLCE_STATIC_SCRATCH_BYTES = 144 << 20  # include/flce.h
 # enum flce_kernel_id of include/flce.h
 KERNEL_NAMES = ["fwd", "fwd_keep", "fwd_combine", "fwd_finalize", "bwd_prep", "dz", "dh", "dh_acc", "dh_final",
                 "dh_acc_final", "dw", "dw_acc", "labels", "keep_to_dz"]
@@ -32,6 +33,8 @@ SIGNATURES = {
     "flce_forward_backward_chunk": (_I32, [_I64, _I64, _I64, _I32, _SZ, _P]),
     "flce_forward_backward": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I32, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
                                      _P]),
+    "flce_forward_backward_static": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I32, _I64, _P, _P, _P, _P, _P, _P, _P,
+                                            _P]),
     "flce_timing_begin": (_I32, [_P, _P, _I32]),
     "flce_timing_end": (_I32, []),
     "flce_status_string": (ctypes.c_char_p, [_I32]),
@@ -193,6 +196,31 @@ def flce_forward_backward(H, W, y, grad_loss, loss, lse, n_valid, dev_status, dH
                                    _ptr(dH), _ptr(dW), _ptr(workspace), workspace.numel(), _stream(stream))
     if st != FLCE_OK:
         raise FlceError(st, "flce_forward_backward")
+
+
+def flce_forward_backward_static(H, W, y, grad_loss, loss, lse, n_valid, dev_status, dH, dW,
+                                 ignore_index=IGNORE_INDEX, stream=None) -> None:
+    """flce_forward_backward in the library's own fixed device array of
+    FLCE_STATIC_SCRATCH_BYTES (no workspace argument, nothing allocated).  Calls that
+    overlap on one GPU share that array and race."""
+    N, D = H.shape
+    V = W.shape[0]
+    _check(H, "H")
+    _check(W, "W", H.dtype, (V, D))
+    _check(y, "y", torch.int64, (N,))
+    if grad_loss is not None:
+        _check(grad_loss, "grad_loss", torch.float32, (1,))
+    _check(loss, "loss", torch.float32, (1,))
+    _check(lse, "lse", torch.float32, (N,))
+    _check(n_valid, "n_valid", torch.int32, (1,))
+    _check(dev_status, "dev_status", torch.int32, (1,))
+    _check(dH, "dH", H.dtype, (N, D))
+    _check(dW, "dW", torch.float32, (V, D))
+    st = lib.flce_forward_backward_static(_ptr(H), _ptr(W), _ptr(y), N, D, V, dtype_code(H.dtype), ignore_index,
+                                          _ptr(grad_loss), _ptr(loss), _ptr(lse), _ptr(n_valid), _ptr(dev_status),
+                                          _ptr(dH), _ptr(dW), _stream(stream))
+    if st != FLCE_OK:
+        raise FlceError(st, "flce_forward_backward_static")
 
 
 # --- cross-entropy over materialised logits (include/flce_ce.h) ----------------------

@@ -60,6 +60,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 
 #include "flce.h"
 #include "flce_plan.h"
@@ -1915,6 +1916,31 @@ flce_status single_pass_impl(const T* H, const T* W, const int64_t* y, const flo
   return launched();
 }
 
+// The workspace of flce_forward_backward_static: a fixed device array of the library's
+// own, for callers that cannot allocate.  Each GPU the library runs on holds its own copy
+// until the process ends.  Host code must not pass `scratch` itself to a kernel (on the host
+// it names a stand-in, not device memory): the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[FLCE_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mutex;
+void* g_scratch_addr[kMaxDevices];
+
+// The current device's address of `scratch` (looked up on the device's first call).
+flce_status static_scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FLCE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FLCE_ERR_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return FLCE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -2047,6 +2073,24 @@ flce_status flce_forward_backward(const void* H, const void* W, const int64_t* y
   if (f != FLCE_OK) return f;
   return flce_backward(H, W, y, lse, n_valid, grad_loss, N, D, V, dtype, ignore_index, dH, dW, workspace,
                        workspace_bytes, stream);
+}
+
+flce_status flce_forward_backward_static(const void* H, const void* W, const int64_t* y, int64_t N, int64_t D,
+                                         int64_t V, int dtype, int64_t ignore_index, const float* grad_loss,
+                                         float* loss, float* lse, int32_t* n_valid, int32_t* dev_status, void* dH,
+                                         float* dW, void* stream) {
+  // Every check that needs no device runs first, so a size beyond the array is reported
+  // before anything touches the GPU.
+  if (!sizes_ok(N, D, V, dtype)) return FLCE_ERR_INVALID_ARG;
+  int64_t tc = 0;
+  const flce_status plan = flce_forward_backward_chunk(N, D, V, dtype, FLCE_STATIC_SCRATCH_BYTES, &tc);
+  if (plan != FLCE_OK) return plan;
+  if (!H || !W || !y || !loss || !lse || !n_valid || !dev_status || !dH || !dW) return FLCE_ERR_INVALID_ARG;
+  void* ws = nullptr;
+  const flce_status a = static_scratch_address(&ws);
+  if (a != FLCE_OK) return a;
+  return flce_forward_backward(H, W, y, N, D, V, dtype, ignore_index, grad_loss, loss, lse, n_valid, dev_status, dH,
+                               dW, ws, FLCE_STATIC_SCRATCH_BYTES, stream);
 }
 
 int32_t flce_timing_begin(void** events, int32_t* kernel_ids, int32_t capacity) {

@@ -290,3 +290,37 @@ def test_forward_backward_argument_errors(B):
     fwd_only = B.flce_workspace_bytes(512, 64, 1024, 1) // 16
     assert _fb(B, wsb=fwd_only) == B.FLCE_ERR_WORKSPACE
 
+
+# --- the entry point that allocates nothing -----------------------------------------
+
+
+def test_static_scratch_size_matches_header(B):
+    text = open(HEADERS[0]).read()
+    m = re.search(r"#define FLCE_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and (int(m.group(1)) << int(m.group(2))) == B.FLCE_STATIC_SCRATCH_BYTES
+    # the default two-call workspace of every workload fits the array
+    for N, D, V, dt in [(16384, 4096, 128256, 1), (8192, 3584, 152064, 1), (4096, 4096, 32000, 1),
+                        (8192, 4096, 32768, 1), (16384, 4096, 128256, 2), (64, 256, 1024, 0)]:
+        assert B.flce_workspace_bytes(N, D, V, dt) <= B.FLCE_STATIC_SCRATCH_BYTES
+        assert B.flce_forward_backward_chunk(N, D, V, dt, B.FLCE_STATIC_SCRATCH_BYTES) >= 0
+
+
+def _fbs(B, H=A16, W=A16, y=A16, N=512, D=64, V=1024, dt=1, g=None, loss=A16, lse=A16, nv=A16, st=A16, dH=A16,
+         dW=A16):
+    return B.lib.flce_forward_backward_static(H, W, y, N, D, V, dt, -100, g, loss, lse, nv, st, dH, dW, None)
+
+
+def test_static_rejects_before_touching_the_device(B):
+    """Sizes beyond the array and invalid arguments are reported without a GPU."""
+    # a vocabulary too wide for the single pass (256 kept rows of 9e6 columns pass the
+    # 32-bit offset limit), and 16M rows whose per-row terms alone (12 bytes a row) exceed
+    # 144 MiB for the recomputing schedule
+    assert B.flce_forward_backward_chunk(16 << 20, 8, 9_000_000, 1, 10**12) == 0
+    assert _fbs(B, N=16 << 20, D=8, V=9_000_000) == B.FLCE_ERR_WORKSPACE
+    # the single pass needs only a few bytes per row besides its kept chunk: 16M rows at a
+    # small vocabulary fit the array
+    assert B.flce_forward_backward_chunk(16 << 20, 8, 8, 1, B.FLCE_STATIC_SCRATCH_BYTES) > 0
+    assert _fbs(B, N=0) == B.FLCE_ERR_INVALID_ARG
+    assert _fbs(B, dt=9) == B.FLCE_ERR_INVALID_ARG
+    assert _fbs(B, H=None) == B.FLCE_ERR_INVALID_ARG
+    assert _fbs(B, dW=None) == B.FLCE_ERR_INVALID_ARG
