@@ -723,6 +723,34 @@ def _time_steps(args, step, stream):
     return ms, fwd_ms, step_ms, peak_delta, clk.summary()
 
 
+def summarize_trace(path: str) -> list[dict]:
+    """Per kernel (full name), from a rocprofv3 --kernel-trace output: dispatches, mean, min
+    and max duration in us and the share of all kernel time.  `path` is the output directory
+    (its *kernel_trace.csv, or else its *results.db) or a results database itself."""
+    import csv
+    import glob
+    import sqlite3
+    durs = {}
+    csvs = glob.glob(os.path.join(path, "**", "*kernel_trace.csv"), recursive=True) if os.path.isdir(path) else []
+    if csvs:
+        for f in csvs:
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    durs.setdefault(r["Kernel_Name"], []).append(
+                        (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+    else:
+        dbs = glob.glob(os.path.join(path, "**", "*results.db"), recursive=True) if os.path.isdir(path) else [path]
+        for db in dbs:
+            con = sqlite3.connect(db)
+            for name, start, end in con.execute("select name, start, end from kernels"):
+                durs.setdefault(name, []).append((end - start) * 1e-3)
+            con.close()
+    total = sum(sum(v) for v in durs.values())
+    out = [{"kernel": k, "dispatches": len(v), "mean_us": sum(v) / len(v), "min_us": min(v), "max_us": max(v),
+            "share": sum(v) / total} for k, v in durs.items()]
+    return sorted(out, key=lambda r: -r["share"])
+
+
 OCCUPANCY_COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT",
                       "SQ_LDS_ADDR_CONFLICT", "SQ_BUSY_CU_CYCLES", "SQ_WAIT_INST_LDS", "SQ_LDS_DATA_FIFO_FULL")
 MI355X_XCDS, MI355X_CUS, MI355X_SIMDS = 8, 256, 1024
@@ -793,6 +821,9 @@ def main() -> int:
     ap.add_argument("--summarize-counters", metavar="DIR",
                     help="only write the path's traffic record from rocprofv3 counter runs under DIR "
                          "(subdirectories F, W, FC, WC); no GPU needed")
+    ap.add_argument("--summarize-trace", metavar="PATH",
+                    help="only print per-kernel dispatch counts and durations from a rocprofv3 --kernel-trace "
+                         "output directory or results database; no GPU needed")
     ap.add_argument("--summarize-occupancy", metavar="DIR",
                     help="only print, per kernel, clock, MFMA-busy and LDS figures from one rocprofv3 --pmc "
                          "run of bench.OCCUPANCY_COUNTERS under DIR; no GPU needed")
@@ -800,6 +831,10 @@ def main() -> int:
     ap.add_argument("--kinds", default=None,
                     help="--summarize-counters: comma-separated kernel kinds (default: the path's GEMMs)")
     args = ap.parse_args()
+    if args.summarize_trace:
+        for rec in summarize_trace(args.summarize_trace):
+            print(json.dumps(rec), flush=True)
+        return 0
     if args.summarize_occupancy:
         for rec in summarize_occupancy(args.summarize_occupancy):
             print(json.dumps(rec), flush=True)
