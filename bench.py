@@ -71,6 +71,7 @@ KINDS = {
     "bwd_dz": ("bwd_dz<", (5,)),
     "bwd_dh": ("bwd_dh<", (6, 7, 8, 9)),
     "bwd_dw": ("bwd_dw<", (10, 11)),
+    "bwd_dhdw": ("bwd_dhdw<", (14,)),
     "keep_to_dz": ("keep_to_dz<", (13,)),
     "ce_rows_bwd": ("ce_rows_bwd", ()),
     "rms_bwd": ("rms_bwd", ()),
@@ -277,19 +278,27 @@ def chunk_spans(total: int, chunk: int) -> list[tuple[int, int]]:
     return out
 
 
-def gemm_launch_flops(path: str, N: int, D: int, V: int, tc: int, vc: int) -> list[tuple[int, float]]:
+def gemm_launch_flops(path: str, N: int, D: int, V: int, tc: int, vc: int,
+                      separate: bool = False) -> list[tuple[int, float]]:
     """(flce_kernel_id, algorithmic flops) of each GEMM launch of one step, in launch order:
-    2 x tokens x vocabulary rows x D of the launch's chunk (the forward: all of N x V)."""
+    2 x tokens x vocabulary rows x D of each contraction the launch runs (the forward: all of
+    N x V).  The recomputing backward runs, per chunk (token chunk, vocabulary chunk), a dz
+    launch and one launch with both dH and dW; `separate`: dH and dW as two launches (the
+    schedule before they were fused)."""
     out = []
     if path == "fused":
         out.append((0, 2.0 * N * V * D))
         tspans, vspans = chunk_spans(N, tc), chunk_spans(V, vc)
         last = len(vspans) - 1
-        for ci, (_, tr) in enumerate(tspans):
-            for vi, (_, vr) in enumerate(vspans):
-                f = 2.0 * tr * vr * D
+        flops = [2.0 * tr * vr * D for _, tr in tspans for _, vr in vspans]
+        if separate:
+            for k, f in enumerate(flops):
+                ci, vi = divmod(k, len(vspans))
                 dh = 6 + (1 if vi > 0 else 0) + (2 if vi == last else 0)
                 out += [(5, f), (dh, f), (11 if ci > 0 else 10, f)]
+        else:
+            for f in flops:
+                out += [(5, f), (14, 2.0 * f)]
     else:  # single pass, token chunks of tc over the whole vocabulary
         for ci in range(-(-N // tc)):
             rows = min(tc, N - ci * tc)
@@ -298,8 +307,8 @@ def gemm_launch_flops(path: str, N: int, D: int, V: int, tc: int, vc: int) -> li
     return out
 
 
-GEMM_KINDS = {"fused": {"f16": ["fwd_tiles16", "bwd_dz16", "bwd_dh", "bwd_dw"],
-                        "f32": ["fwd_tiles", "bwd_dz", "bwd_dh", "bwd_dw"]},
+GEMM_KINDS = {"fused": {"f16": ["fwd_tiles16", "bwd_dz16", "bwd_dhdw", "bwd_dh", "bwd_dw"],
+                        "f32": ["fwd_tiles", "bwd_dz", "bwd_dhdw", "bwd_dh", "bwd_dw"]},
               "single": {"f16": ["fwd_tiles16_keep", "bwd_dh", "bwd_dw"],
                          "f32": ["fwd_tiles_keep", "bwd_dh", "bwd_dw"]}}
 
@@ -311,7 +320,7 @@ def time_launches(args, B, step, stream, path: str, cfg, tc: int, vc: int) -> di
     region's step time; checks that the launches ran in the order the chunking implies."""
     import ctypes
     import torch
-    expect = gemm_launch_flops(path, cfg.N, cfg.D, cfg.V, tc, vc)
+    expect = gemm_launch_flops(path, cfg.N, cfg.D, cfg.V, tc, vc, separate=True)
     cap = args.steps * (len(expect) + 16)
     ev = HipEvents(2 * cap)
     ids = (ctypes.c_int32 * cap)()
@@ -327,9 +336,14 @@ def time_launches(args, B, step, stream, path: str, cfg, tc: int, vc: int) -> di
     finally:
         n = B.lib.flce_timing_end()
     torch.cuda.synchronize()
-    gemm_ids = {k for k, _ in expect}
-    got = [(ids[i], ev.elapsed_ms(2 * i, 2 * i + 1)) for i in range(n) if ids[i] in gemm_ids]
+    gemm = {0, 1, 5, 6, 7, 8, 9, 10, 11, 14}
+    got = [(ids[i], ev.elapsed_ms(2 * i, 2 * i + 1)) for i in range(n) if ids[i] in gemm]
     ev.close()
+    if path == "fused":  # which of the schedules the library took
+        for cand in (dict(separate=False), dict(separate=True)):
+            expect = gemm_launch_flops(path, cfg.N, cfg.D, cfg.V, tc, vc, **cand)
+            if [k for k, _ in got] == [k for k, _ in expect] * args.steps:
+                break
     if [k for k, _ in got] != [k for k, _ in expect] * args.steps:
         raise RuntimeError("GEMM launches did not follow the expected chunk order")
     family = "f32" if cfg.dtype == "f32" else "f16"
@@ -337,6 +351,8 @@ def time_launches(args, B, step, stream, path: str, cfg, tc: int, vc: int) -> di
     for kind in GEMM_KINDS[path][family]:
         kid = set(KINDS[kind][1])
         durs = [d for (k, d) in got if k in kid]
+        if not durs:
+            continue
         flops = [f for (k, f) in expect if k in kid] * args.steps
         mean_ms = sum(durs) / len(durs)
         mean_flop = sum(flops) / len(flops)
@@ -841,7 +857,7 @@ def main() -> int:
         return 0
     if args.summarize_counters:
         kinds = args.kinds.split(",") if args.kinds else {
-            "fused": ["fwd_tiles16", "bwd_dz16", "bwd_dh", "bwd_dw"], "single": ["fwd_tiles16_keep", "bwd_dh", "bwd_dw"],
+            "fused": ["fwd_tiles16", "bwd_dz16", "bwd_dhdw"], "single": ["fwd_tiles16_keep", "bwd_dh", "bwd_dw"],
             "ce": ["ce_rows_bwd"], "norm": ["rms_bwd"]}[args.path]
         for rec in summarize_counters(args.summarize_counters, args.copy_bytes, args.path, kinds,
                                       args.workload or PATHS[args.path][0]):

@@ -245,7 +245,8 @@ enum flce_kernel_id {
   FLCE_KERNEL_DW = 10,           /* dW of the first token chunk (stored) */
   FLCE_KERNEL_DW_ACC = 11,       /* dW of a later token chunk, added in place */
   FLCE_KERNEL_LABELS = 12,       /* N_valid before any chunk (single pass) */
-  FLCE_KERNEL_KEEP_TO_DZ = 13    /* kept exponentials -> dz slab (single pass) */
+  FLCE_KERNEL_KEEP_TO_DZ = 13,   /* kept exponentials -> dz slab (single pass) */
+  FLCE_KERNEL_DHDW = 14          /* dH and dW of one chunk in one launch */
 };
 
 /*

@@ -1306,12 +1306,10 @@ template <> __device__ __forceinline__ void store4_signed<float>(float* p, const
 // dz tiles of one (vocab chunk, token chunk); slab is [token in chunk][vocab in chunk].
 // Persistent: tile b = (vt, tt) in the order of tile_rc, handed out round-robin.
 template <typename T>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dz(const T* __restrict__ H, const T* __restrict__ W, int D,
-                                                       int v0c, int vc_act, int t0c, int tc_act, int n_tiles_t,
-                                                       const float* __restrict__ e2, const float* __restrict__ coef,
-                                                       const int* __restrict__ lab, T* __restrict__ slab,
-                                                       int ld_slab) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+__device__ __forceinline__ void dz_body(char* lds, const T* __restrict__ H, const T* __restrict__ W, int D, int v0c,
+                                        int vc_act, int t0c, int tc_act, int n_tiles_t, const float* __restrict__ e2,
+                                        const float* __restrict__ coef, const int* __restrict__ lab,
+                                        T* __restrict__ slab, int ld_slab) {
   const int ldb = D * (int)sizeof(T);
   const int tiles = ((vc_act + kTile - 1) / kTile) * n_tiles_t;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1384,21 +1382,29 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dz(const T* __restrict__ H, c
       }
     }
   };
-  gemm_run<T>(lds, my_tile_count(tiles), even_slices<T>(D), mk, epi);
+  const int count = my_tile_count(tiles);
+  if (count > 0) gemm_run<T>(lds, count, even_slices<T>(D), mk, epi);
+}
+template <typename T>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dz(const T* __restrict__ H, const T* __restrict__ W, int D,
+                                                       int v0c, int vc_act, int t0c, int tc_act, int n_tiles_t,
+                                                       const float* __restrict__ e2, const float* __restrict__ coef,
+                                                       const int* __restrict__ lab, T* __restrict__ slab,
+                                                       int ld_slab) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  dz_body<T>(lds, H, W, D, v0c, vc_act, t0c, tc_act, n_tiles_t, e2, coef, lab, slab, ld_slab);
 }
 
 // bwd_dz on the 16 x 16 x 32 core (16-bit T): same tiles, order and slab layout.  A lane
 // holds four consecutive vocabulary rows of one token per 16-row block, so each block
 // becomes one 8-byte store.
 template <typename T>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dz16(const T* __restrict__ H, const T* __restrict__ W, int D,
-                                                         int v0c, int vc_act, int t0c, int tc_act, int n_tiles_t,
-                                                         const float* __restrict__ e2, const float* __restrict__ coef,
-                                                         const int* __restrict__ lab, T* __restrict__ slab,
-                                                         int ld_slab) {
+__device__ __forceinline__ void dz16_body(char* lds, const T* __restrict__ H, const T* __restrict__ W, int D, int v0c,
+                                          int vc_act, int t0c, int tc_act, int n_tiles_t,
+                                          const float* __restrict__ e2, const float* __restrict__ coef,
+                                          const int* __restrict__ lab, T* __restrict__ slab, int ld_slab) {
   using c16::kBM;
   using c16::kBN;
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   const int ldb = D * (int)sizeof(T);
   const int tiles = ((vc_act + kTile - 1) / kTile) * n_tiles_t;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1456,7 +1462,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dz16(const T* __restrict__ H,
       }
     }
   };
-  c16::gemm_run<T>(lds, my_tile_count(tiles), even_slices<T>(D), mk, epi);
+  const int count = my_tile_count(tiles);
+  if (count > 0) c16::gemm_run<T>(lds, count, even_slices<T>(D), mk, epi);
+}
+template <typename T>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dz16(const T* __restrict__ H, const T* __restrict__ W, int D,
+                                                         int v0c, int vc_act, int t0c, int tc_act, int n_tiles_t,
+                                                         const float* __restrict__ e2, const float* __restrict__ coef,
+                                                         const int* __restrict__ lab, T* __restrict__ slab,
+                                                         int ld_slab) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  dz16_body<T>(lds, H, W, D, v0c, vc_act, t0c, tc_act, n_tiles_t, e2, coef, lab, slab, ld_slab);
 }
 
 template <typename TO> __device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, u32 off, float v);
@@ -1527,12 +1543,10 @@ __device__ __forceinline__ void tile_out(const f32x16 (&acc)[kBM][kBN], const fl
 // b = (mt, dt) in the order of tile_rc.  ACCUM: add the fp32 partial in dacc;
 // FINAL: write the sum to dH in the output type instead of back to dacc.
 template <typename T, bool ACCUM, bool FINAL>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dh(const T* __restrict__ slab, int ld_slab,
-                                                       const T* __restrict__ W, int D, int v0c, int vc_act,
-                                                       int t0c, int tc_act, int n_tiles_d,
-                                                       float* __restrict__ dacc, T* __restrict__ dH,
-                                                       const float* __restrict__ oscale) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+__device__ __forceinline__ void dh_body(char* lds, const T* __restrict__ slab, int ld_slab, const T* __restrict__ W,
+                                        int D, int v0c, int vc_act, int t0c, int tc_act, int n_tiles_d,
+                                        float* __restrict__ dacc, T* __restrict__ dH,
+                                        const float* __restrict__ oscale) {
   const float sc = oscale ? *oscale : 1.f;
   const int es = (int)sizeof(T);
   const int tiles = ((tc_act + kTile - 1) / kTile) * n_tiles_d;
@@ -1555,17 +1569,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh(const T* __restrict__ slab
     else
       tile_out<float>(acc, prev, acc_tile, D, tc_act - nl0, D - d0, sc);
   };
-  gemm_run<T>(lds, my_tile_count(tiles), even_slices<T>(vc_act), mk, epi);
+  const int count = my_tile_count(tiles);
+  if (count > 0) gemm_run<T>(lds, count, even_slices<T>(vc_act), mk, epi);
+}
+template <typename T, bool ACCUM, bool FINAL>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dh(const T* __restrict__ slab, int ld_slab,
+                                                       const T* __restrict__ W, int D, int v0c, int vc_act,
+                                                       int t0c, int tc_act, int n_tiles_d,
+                                                       float* __restrict__ dacc, T* __restrict__ dH,
+                                                       const float* __restrict__ oscale) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  dh_body<T, ACCUM, FINAL>(lds, slab, ld_slab, W, D, v0c, vc_act, t0c, tc_act, n_tiles_d, dacc, dH, oscale);
 }
 
 // dW rows of one vocab chunk (+)= slab^T x H[token chunk]; C[v][d].  Persistent over tiles
 // b = (vt, dt) in the order of tile_rc.
 template <typename T, bool ACCUM>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dw(const T* __restrict__ slab, int ld_slab,
-                                                       const T* __restrict__ H, int D, int t0c, int tc_act,
-                                                       int v0c, int vc_act, int n_tiles_d, float* __restrict__ dW,
-                                                       const float* __restrict__ oscale) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+__device__ __forceinline__ void dw_body(char* lds, const T* __restrict__ slab, int ld_slab, const T* __restrict__ H,
+                                        int D, int t0c, int tc_act, int v0c, int vc_act, int n_tiles_d,
+                                        float* __restrict__ dW, const float* __restrict__ oscale) {
   const float sc = oscale ? *oscale : 1.f;
   const int es = (int)sizeof(T);
   const int tiles = ((vc_act + kTile - 1) / kTile) * n_tiles_d;
@@ -1584,7 +1606,41 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dw(const T* __restrict__ slab
     float* tile = dW + (int64_t)(v0c + vl0) * D + d0;
     tile_out<float>(acc, ACCUM ? tile : nullptr, tile, D, vc_act - vl0, D - d0, sc);
   };
-  gemm_run<T>(lds, my_tile_count(tiles), even_slices<T>(tc_act), mk, epi);
+  const int count = my_tile_count(tiles);
+  if (count > 0) gemm_run<T>(lds, count, even_slices<T>(tc_act), mk, epi);
+}
+template <typename T, bool ACCUM>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dw(const T* __restrict__ slab, int ld_slab,
+                                                       const T* __restrict__ H, int D, int t0c, int tc_act,
+                                                       int v0c, int vc_act, int n_tiles_d, float* __restrict__ dW,
+                                                       const float* __restrict__ oscale) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  dw_body<T, ACCUM>(lds, slab, ld_slab, H, D, t0c, tc_act, v0c, vc_act, n_tiles_d, dW, oscale);
+}
+
+// dH and dW of one (token chunk, vocabulary chunk) in one launch: both contract the same dz
+// slab and write different outputs, so each workgroup runs its share of the dH tiles and of
+// the dW tiles back to back, odd workgroups dW first.  One launch instead of two spares a
+// pipeline fill and drain, and half the workgroups reach their read-modify-write epilogues
+// at other times than the rest (measured 2% faster per step than two launches).  The
+// barrier between the halves lets every wave drain its trailing loads into LDS before the
+// next half loads into the same stages.
+template <typename T, bool DH_ACC, bool DH_FIN, bool DW_ACC>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dhdw(const T* __restrict__ slab, int ld_slab,
+                                                         const T* __restrict__ W, const T* __restrict__ H, int D,
+                                                         int v0c, int vc_act, int t0c, int tc_act, int n_tiles_d,
+                                                         float* __restrict__ dacc, T* __restrict__ dH,
+                                                         float* __restrict__ dW, const float* __restrict__ oscale) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  if (blockIdx.x & 1) {
+    dw_body<T, DW_ACC>(lds, slab, ld_slab, H, D, t0c, tc_act, v0c, vc_act, n_tiles_d, dW, oscale);
+    __syncthreads();
+    dh_body<T, DH_ACC, DH_FIN>(lds, slab, ld_slab, W, D, v0c, vc_act, t0c, tc_act, n_tiles_d, dacc, dH, oscale);
+  } else {
+    dh_body<T, DH_ACC, DH_FIN>(lds, slab, ld_slab, W, D, v0c, vc_act, t0c, tc_act, n_tiles_d, dacc, dH, oscale);
+    __syncthreads();
+    dw_body<T, DW_ACC>(lds, slab, ld_slab, H, D, t0c, tc_act, v0c, vc_act, n_tiles_d, dW, oscale);
+  }
 }
 
 // ---------------------------------------------------------------------------------
@@ -1790,7 +1846,6 @@ flce_status backward_impl(const T* H, const T* W, const int64_t* y, const float*
   float* e2 = reinterpret_cast<float*>(ws + L.e2);
   float* coef = reinterpret_cast<float*>(ws + L.coef);
   int* lab = reinterpret_cast<int*>(ws + L.lab);
-  T* slab = reinterpret_cast<T*>(ws + L.slab);
   float* dacc = dtype != FLCE_F32 ? reinterpret_cast<float*>(ws + L.dacc) : nullptr;
   // fp16 slabs hold dz scaled by 2^14 / |g / N_valid| (dz itself is far below fp16's range
   // at large N), undone by the dH and dW epilogues.
@@ -1806,6 +1861,15 @@ flce_status backward_impl(const T* H, const T* W, const int64_t* y, const float*
   const int n_tc = (int)ceil_div(N, L.tc), n_vc = (int)ceil_div(V, L.vc);
   const int64_t t_tiles = ceil_div(N, kTile), v_tiles = ceil_div(V, kTile);
   auto grid = [](int tiles) { return (unsigned)(tiles < kPersistentWGs ? tiles : kPersistentWGs); };
+  T* slab = reinterpret_cast<T*>(ws + L.slab);
+  // bwd_dhdw's variant: whether dH adds to an earlier vocabulary chunk's partial, converts it
+  // to the output type, and whether dW adds to an earlier token chunk's.
+  using DhDw = void (*)(const T*, int, const T*, const T*, int, int, int, int, int, int, float*, T*, float*,
+                        const float*);
+  static constexpr DhDw kDhDw[8] = {bwd_dhdw<T, false, false, false>, bwd_dhdw<T, true, false, false>,
+                                    bwd_dhdw<T, false, true, false>,  bwd_dhdw<T, true, true, false>,
+                                    bwd_dhdw<T, false, false, true>,  bwd_dhdw<T, true, false, true>,
+                                    bwd_dhdw<T, false, true, true>,   bwd_dhdw<T, true, true, true>};
   for (int ci = 0; ci < n_tc; ++ci) {
     const int t0c = (int)(ci * t_tiles / n_tc * kTile);
     const int t1c = (int)((ci + 1) * t_tiles / n_tc * kTile);
@@ -1819,29 +1883,15 @@ flce_status backward_impl(const T* H, const T* W, const int64_t* y, const float*
       const int vc_act = (v1c < V ? v1c : V) - v0c;
       const int n_vt = (int)ceil_div(vc_act, kTile);
       if constexpr (sizeof(T) == 2)
-        launch(FLCE_KERNEL_DZ, bwd_dz16<T>, dim3(grid(n_vt * n_tt)), dim3(kThreads), s, H, W, D, v0c, vc_act, t0c, tc_act, n_tt,
-                                                                       e2, coef, lab, slab, ld_slab);
+        launch(FLCE_KERNEL_DZ, bwd_dz16<T>, dim3(grid(n_vt * n_tt)), dim3(kThreads), s, H, W, D, v0c, vc_act, t0c,
+               tc_act, n_tt, e2, coef, lab, slab, ld_slab);
       else
-        launch(FLCE_KERNEL_DZ, bwd_dz<T>, dim3(grid(n_vt * n_tt)), dim3(kThreads), s, H, W, D, v0c, vc_act, t0c, tc_act, n_tt, e2,
-                                                                     coef, lab, slab, ld_slab);
-      const dim3 gh(grid(n_tt * n_td)), gw(grid(n_vt * n_td)), blk(kThreads);
-      const bool acc_dh = vi > 0, fin = dacc && vi == n_vc - 1;
-      if (!acc_dh && !fin)
-        launch(FLCE_KERNEL_DH, bwd_dh<T, false, false>, gh, blk, s, slab, ld_slab, W, D, v0c, vc_act, t0c, tc_act, n_td, acc_rows, dH,
-                                                oscale);
-      else if (acc_dh && !fin)
-        launch(FLCE_KERNEL_DH_ACC, bwd_dh<T, true, false>, gh, blk, s, slab, ld_slab, W, D, v0c, vc_act, t0c, tc_act, n_td, acc_rows, dH,
-                                                oscale);
-      else if (!acc_dh && fin)
-        launch(FLCE_KERNEL_DH_FINAL, bwd_dh<T, false, true>, gh, blk, s, slab, ld_slab, W, D, v0c, vc_act, t0c, tc_act, n_td, acc_rows, dH,
-                                                oscale);
-      else
-        launch(FLCE_KERNEL_DH_ACC_FINAL, bwd_dh<T, true, true>, gh, blk, s, slab, ld_slab, W, D, v0c, vc_act, t0c, tc_act, n_td, acc_rows, dH,
-                                                oscale);
-      if (ci > 0)
-        launch(FLCE_KERNEL_DW_ACC, bwd_dw<T, true>, gw, blk, s, slab, ld_slab, H, D, t0c, tc_act, v0c, vc_act, n_td, dW, oscale);
-      else
-        launch(FLCE_KERNEL_DW, bwd_dw<T, false>, gw, blk, s, slab, ld_slab, H, D, t0c, tc_act, v0c, vc_act, n_td, dW, oscale);
+        launch(FLCE_KERNEL_DZ, bwd_dz<T>, dim3(grid(n_vt * n_tt)), dim3(kThreads), s, H, W, D, v0c, vc_act, t0c,
+               tc_act, n_tt, e2, coef, lab, slab, ld_slab);
+      const bool acc_dh = vi > 0, fin = dacc && vi == n_vc - 1, acc_dw = ci > 0;
+      const int tiles = n_tt > n_vt ? n_tt * n_td : n_vt * n_td;
+      launch(FLCE_KERNEL_DHDW, kDhDw[(acc_dh ? 1 : 0) + (fin ? 2 : 0) + (acc_dw ? 4 : 0)], dim3(grid(tiles)),
+             dim3(kThreads), s, slab, ld_slab, W, H, D, v0c, vc_act, t0c, tc_act, n_td, acc_rows, dH, dW, oscale);
     }
   }
   return launched();

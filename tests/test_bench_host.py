@@ -93,18 +93,21 @@ def test_chunk_spans_partition_whole_tiles():
     assert bench.chunk_spans(128256, 8192)[0] == (0, 7936)  # 501 tiles over 16 chunks: 31 or 32 tiles
 
 
-@pytest.mark.parametrize("path,tc,vc", [("fused", 4096, 8192), ("single", 4096, 0), ("single", 8192, 0)])
-def test_gemm_launch_flops_cover_each_kind_once(path, tc, vc):
-    """Every GEMM kind's launches add up to one full 2 N V D contraction per step."""
+@pytest.mark.parametrize("path,tc,vc,mode", [("fused", 4096, 8192, "separate"), ("fused", 4096, 8192, "dhdw"),
+                                              ("single", 4096, 0, None), ("single", 8192, 0, None)])
+def test_gemm_launch_flops_cover_the_work_once(path, tc, vc, mode):
+    """The GEMM launches of a step add up to the forward (2 N V D, or none for a single
+    pass's separate kinds) plus three 2 N V D contractions of the backward."""
     N, D, V = 16384, 4096, 128256
-    launches = bench.gemm_launch_flops(path, N, D, V, tc, vc)
-    family = bench.GEMM_KINDS[path]["f16"]
-    for kind in family:
-        ids = set(bench.KINDS[kind][1])
-        assert sum(f for k, f in launches if k in ids) == pytest.approx(2.0 * N * V * D)
-    if path == "fused":
+    kw = {} if mode is None else dict(separate=mode == "separate")
+    launches = bench.gemm_launch_flops(path, N, D, V, tc, vc, **kw)
+    assert sum(f for _, f in launches) == pytest.approx((4.0 if path == "fused" else 3.0) * 2.0 * N * V * D)
+    if mode == "separate":
         assert len(launches) == 1 + 3 * 4 * 16
         assert [k for k, _ in launches[1:4]] == [5, 6, 10] and [k for k, _ in launches[-3:]] == [5, 9, 11]
+    elif mode == "dhdw":
+        assert [k for k, _ in launches] == [0] + [5, 14] * 64
+        assert launches[2][1] == pytest.approx(2 * launches[1][1])
     else:
         assert len(launches) == 3 * (N // tc)
 
