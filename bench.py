@@ -321,7 +321,7 @@ def time_launches(args, B, step, stream, path: str, cfg, tc: int, vc: int) -> di
     import ctypes
     import torch
     expect = gemm_launch_flops(path, cfg.N, cfg.D, cfg.V, tc, vc, separate=True)
-    cap = args.steps * (len(expect) + 16)
+    cap = args.steps * (3 * len(expect) + 64)  # every launch takes a pair, the small kernels too
     ev = HipEvents(2 * cap)
     ids = (ctypes.c_int32 * cap)()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -643,6 +643,43 @@ def run_norm(args) -> dict:
     return out
 
 
+def run_unfused_memory(args) -> dict:
+    """The pages' memory experiment, as context: peak device memory (torch's
+    max_memory_allocated, above what is held before) of the unfused head -- logits H W^T
+    materialised in the input type, F.cross_entropy, autograd's backward into H and W --
+    beside the fused library's whole workspace, on the Llama-2- and Llama-3-shaped
+    workloads.  Plain 2-D products only.  One line per workload; no timing."""
+    import torch
+    import torch.nn.functional as F
+    from linear_cross_entropy_lm_amd import binding as B
+    from linear_cross_entropy_lm_amd import inputs as I
+    out = []
+    for name in (args.workload or "llama2,llama3").split(","):
+        cfg = I.CONFIGS[name]
+        inp = I.generate(cfg)
+        H, W, y = inp.device_tensors("cuda:0")
+        H.requires_grad_(True)
+        W.requires_grad_(True)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        held = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        loss = F.cross_entropy(torch.mm(H, W.t()), y, ignore_index=-100)
+        loss.backward()
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - held
+        grads = H.grad.numel() * H.grad.element_size() + W.grad.numel() * W.grad.element_size()
+        ws = B.flce_workspace_bytes(cfg.N, cfg.D, cfg.V, H.dtype)
+        logit_bytes = cfg.N * cfg.V * H.element_size()
+        out.append({"workload": name, "N": cfg.N, "D": cfg.D, "V": cfg.V, "dtype": cfg.dtype,
+                    "unfused_peak_bytes": int(peak), "unfused_peak_minus_grads": int(peak - grads),
+                    "logit_bytes": int(logit_bytes), "fused_workspace_bytes": int(ws),
+                    "fused_workspace_frac_of_logits": ws / logit_bytes, "loss": float(loss.item())})
+        del H, W, y, loss
+        torch.cuda.empty_cache()
+    return {"memory": out}
+
+
 def _parse_sclk_mhz(text: str):
     """The current level of an amdgpu pp_dpm_sclk listing ("1: 1650Mhz *") in MHz, or None."""
     import re
@@ -821,7 +858,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--path", choices=sorted(PATHS), default="fused",
+    ap.add_argument("--path", choices=sorted(PATHS) + ["unfused-memory"], default="fused",
                     help="fused: lm_head projection + cross-entropy (default); single: the same in one "
                          "call without logit recompute (25%% scratch); ce: cross-entropy over materialised "
                          "logits; norm: the RMSNorm that produces H")
@@ -876,7 +913,8 @@ def main() -> int:
         print(f"bench.py: this build runs on exactly one GPU (asked for {args.gpus}); the multi-GPU "
               "sharding of the path is described, not built.", file=sys.stderr)
         return 2
-    out = {"ce": run_ce, "norm": run_norm, "single": run_single, "fused": run_fused}[args.path](args)
+    out = {"ce": run_ce, "norm": run_norm, "single": run_single, "fused": run_fused,
+           "unfused-memory": run_unfused_memory}[args.path](args)
     print(json.dumps(out), flush=True)
     return 0
 
