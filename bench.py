@@ -69,10 +69,8 @@ KINDS = {
     "fwd_tiles_keep": (r"fwd_tiles<[^<>]*, true>", (1,)),
     "bwd_dz16": ("bwd_dz16<", (5,)),
     "bwd_dz": ("bwd_dz<", (5,)),
-    "bwd_dh": ("bwd_dh<", (6, 7, 8, 9)),
-    "bwd_dw": ("bwd_dw<", (10, 11)),
-    "bwd_dhdw": ("bwd_dhdw<", (14,)),
-    "keep_to_dz": ("keep_to_dz<", (13,)),
+    "bwd_dhdw": ("bwd_dhdw<", (6,)),
+    "keep_to_dz": ("keep_to_dz<", (8,)),
     "ce_rows_bwd": ("ce_rows_bwd", ()),
     "rms_bwd": ("rms_bwd", ()),
 }
@@ -278,39 +276,28 @@ def chunk_spans(total: int, chunk: int) -> list[tuple[int, int]]:
     return out
 
 
-def gemm_launch_flops(path: str, N: int, D: int, V: int, tc: int, vc: int,
-                      separate: bool = False) -> list[tuple[int, float]]:
+def gemm_launch_flops(path: str, N: int, D: int, V: int, tc: int, vc: int) -> list[tuple[int, float]]:
     """(flce_kernel_id, algorithmic flops) of each GEMM launch of one step, in launch order:
-    2 x tokens x vocabulary rows x D of each contraction the launch runs (the forward: all of
-    N x V).  The recomputing backward runs, per chunk (token chunk, vocabulary chunk), a dz
-    launch and one launch with both dH and dW; `separate`: dH and dW as two launches (the
-    schedule before they were fused)."""
+    2 x tokens x vocabulary rows x D of each contraction the launch runs.  The recomputing
+    path: the forward over all of N x V, then per chunk (token chunk, vocabulary chunk) a dz
+    launch and one launch with both dH and dW.  The single pass: per token chunk of tc rows,
+    the keep forward and one launch with dH (K = V) and dW."""
     out = []
     if path == "fused":
         out.append((0, 2.0 * N * V * D))
-        tspans, vspans = chunk_spans(N, tc), chunk_spans(V, vc)
-        last = len(vspans) - 1
-        flops = [2.0 * tr * vr * D for _, tr in tspans for _, vr in vspans]
-        if separate:
-            for k, f in enumerate(flops):
-                ci, vi = divmod(k, len(vspans))
-                dh = 6 + (1 if vi > 0 else 0) + (2 if vi == last else 0)
-                out += [(5, f), (dh, f), (11 if ci > 0 else 10, f)]
-        else:
-            for f in flops:
-                out += [(5, f), (14, 2.0 * f)]
+        for _, tr in chunk_spans(N, tc):
+            for _, vr in chunk_spans(V, vc):
+                f = 2.0 * tr * vr * D
+                out += [(5, f), (6, 2.0 * f)]
     else:  # single pass, token chunks of tc over the whole vocabulary
         for ci in range(-(-N // tc)):
-            rows = min(tc, N - ci * tc)
-            f = 2.0 * rows * V * D
-            out += [(1, f), (8, f), (11 if ci > 0 else 10, f)]
+            f = 2.0 * min(tc, N - ci * tc) * V * D
+            out += [(1, f), (6, 2.0 * f)]
     return out
 
 
-GEMM_KINDS = {"fused": {"f16": ["fwd_tiles16", "bwd_dz16", "bwd_dhdw", "bwd_dh", "bwd_dw"],
-                        "f32": ["fwd_tiles", "bwd_dz", "bwd_dhdw", "bwd_dh", "bwd_dw"]},
-              "single": {"f16": ["fwd_tiles16_keep", "bwd_dh", "bwd_dw"],
-                         "f32": ["fwd_tiles_keep", "bwd_dh", "bwd_dw"]}}
+GEMM_KINDS = {"fused": {"f16": ["fwd_tiles16", "bwd_dz16", "bwd_dhdw"], "f32": ["fwd_tiles", "bwd_dz", "bwd_dhdw"]},
+              "single": {"f16": ["fwd_tiles16_keep", "bwd_dhdw"], "f32": ["fwd_tiles_keep", "bwd_dhdw"]}}
 
 
 def time_launches(args, B, step, stream, path: str, cfg, tc: int, vc: int) -> dict:
@@ -320,7 +307,7 @@ def time_launches(args, B, step, stream, path: str, cfg, tc: int, vc: int) -> di
     region's step time; checks that the launches ran in the order the chunking implies."""
     import ctypes
     import torch
-    expect = gemm_launch_flops(path, cfg.N, cfg.D, cfg.V, tc, vc, separate=True)
+    expect = gemm_launch_flops(path, cfg.N, cfg.D, cfg.V, tc, vc)
     cap = args.steps * (3 * len(expect) + 64)  # every launch takes a pair, the small kernels too
     ev = HipEvents(2 * cap)
     ids = (ctypes.c_int32 * cap)()
@@ -336,14 +323,9 @@ def time_launches(args, B, step, stream, path: str, cfg, tc: int, vc: int) -> di
     finally:
         n = B.lib.flce_timing_end()
     torch.cuda.synchronize()
-    gemm = {0, 1, 5, 6, 7, 8, 9, 10, 11, 14}
+    gemm = {k for k, _ in expect}
     got = [(ids[i], ev.elapsed_ms(2 * i, 2 * i + 1)) for i in range(n) if ids[i] in gemm]
     ev.close()
-    if path == "fused":  # which of the schedules the library took
-        for cand in (dict(separate=False), dict(separate=True)):
-            expect = gemm_launch_flops(path, cfg.N, cfg.D, cfg.V, tc, vc, **cand)
-            if [k for k, _ in got] == [k for k, _ in expect] * args.steps:
-                break
     if [k for k, _ in got] != [k for k, _ in expect] * args.steps:
         raise RuntimeError("GEMM launches did not follow the expected chunk order")
     family = "f32" if cfg.dtype == "f32" else "f16"
@@ -413,7 +395,7 @@ def run_fused(args) -> dict:
     if int(st.item()) != 0:
         raise RuntimeError("dev_status reports invalid labels")
     tc, vc = B.flce_backward_chunks(N, D, V, H.dtype, ws_bytes)
-    timing = time_launches(args, B, step, stream, "fused", cfg, tc, vc)
+    timing = None if args.no_kernel_timing else time_launches(args, B, step, stream, "fused", cfg, tc, vc)
 
     flop_step = 8.0 * N * V * D
     out = _common(args, METRIC, N / (ms * 1e-3), ms, cfg.dtype,
@@ -435,9 +417,9 @@ def run_fused(args) -> dict:
         "scratch_frac_of_unfused_logits": scratch_fraction(ws_bytes, N, V),
         "loss": float(loss.item()),
         "chunks": {"token": tc, "vocab": vc},
-        "kernels": timing["kernels"],
-        "kernel_timing_step_ms": timing["step_ms"],
-        "roofline": gemm_roofline(timing, cfg.name, "fused"),
+        "kernels": timing and timing["kernels"],
+        "kernel_timing_step_ms": timing and timing["step_ms"],
+        "roofline": timing and gemm_roofline(timing, cfg.name, "fused"),
         "cpu_baseline": None,
     })
     if not args.no_cpu_baseline:
@@ -480,7 +462,7 @@ def run_single(args) -> dict:
     tc = B.flce_forward_backward_chunk(N, D, V, H.dtype, ws_bytes)
     if tc == 0:
         raise RuntimeError("the workspace does not buy the single-pass schedule")
-    timing = time_launches(args, B, step, stream, "single", cfg, tc, 0)
+    timing = None if args.no_kernel_timing else time_launches(args, B, step, stream, "single", cfg, tc, 0)
     flop_credit = 8.0 * N * V * D
     out = _common(args, METRIC_SINGLE, N / (ms * 1e-3), ms, cfg.dtype,
                   "synthetic: seeded Gaussian H with unit-RMS rows, W ~ N(0, 0.02^2), uniform labels, "
@@ -499,9 +481,9 @@ def run_single(args) -> dict:
         "scratch_frac_of_unfused_logits": scratch_fraction(ws_bytes, N, V),
         "loss": float(loss.item()),
         "token_chunk": tc,
-        "kernels": timing["kernels"],
-        "kernel_timing_step_ms": timing["step_ms"],
-        "roofline": gemm_roofline(timing, cfg.name, "single"),
+        "kernels": timing and timing["kernels"],
+        "kernel_timing_step_ms": timing and timing["step_ms"],
+        "roofline": timing and gemm_roofline(timing, cfg.name, "single"),
         "cpu_baseline": None,
     })
     if not args.no_cpu_baseline:
@@ -869,6 +851,8 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=None,
                     help="rows of the oracle sample (default 1024 fused, 8192 ce: 10-20 s of CPU work)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true",
+                    help="skip the second timed region with per-launch events (no per-kernel list, no roofline)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run one device-to-device copy of BYTES bytes (counter calibration)")
     ap.add_argument("--summarize-counters", metavar="DIR",
@@ -894,7 +878,7 @@ def main() -> int:
         return 0
     if args.summarize_counters:
         kinds = args.kinds.split(",") if args.kinds else {
-            "fused": ["fwd_tiles16", "bwd_dz16", "bwd_dhdw"], "single": ["fwd_tiles16_keep", "bwd_dh", "bwd_dw"],
+            "fused": ["fwd_tiles16", "bwd_dz16", "bwd_dhdw"], "single": ["fwd_tiles16_keep", "bwd_dhdw"],
             "ce": ["ce_rows_bwd"], "norm": ["rms_bwd"]}[args.path]
         for rec in summarize_counters(args.summarize_counters, args.copy_bytes, args.path, kinds,
                                       args.workload or PATHS[args.path][0]):

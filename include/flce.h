@@ -238,15 +238,9 @@ enum flce_kernel_id {
   FLCE_KERNEL_FWD_FINALIZE = 3,  /* loss, N_valid, status */
   FLCE_KERNEL_BWD_PREP = 4,      /* per-row terms of dz */
   FLCE_KERNEL_DZ = 5,            /* recomputed logit tiles -> dz slab */
-  FLCE_KERNEL_DH = 6,            /* dH partial of the first vocabulary chunk (stored) */
-  FLCE_KERNEL_DH_ACC = 7,        /* dH partial added to the fp32 accumulator */
-  FLCE_KERNEL_DH_FINAL = 8,      /* dH of a single vocabulary chunk, written in the output type */
-  FLCE_KERNEL_DH_ACC_FINAL = 9,  /* last vocabulary chunk: accumulated and written out */
-  FLCE_KERNEL_DW = 10,           /* dW of the first token chunk (stored) */
-  FLCE_KERNEL_DW_ACC = 11,       /* dW of a later token chunk, added in place */
-  FLCE_KERNEL_LABELS = 12,       /* N_valid before any chunk (single pass) */
-  FLCE_KERNEL_KEEP_TO_DZ = 13,   /* kept exponentials -> dz slab (single pass) */
-  FLCE_KERNEL_DHDW = 14          /* dH and dW of one chunk in one launch */
+  FLCE_KERNEL_DHDW = 6,          /* dH and dW of one chunk, contracted from its dz slab */
+  FLCE_KERNEL_LABELS = 7,        /* N_valid before any chunk (single pass) */
+  FLCE_KERNEL_KEEP_TO_DZ = 8     /* kept exponentials -> dz slab (single pass) */
 };
 
 /*

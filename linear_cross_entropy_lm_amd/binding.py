@@ -18,8 +18,7 @@ FLCE_OK, FLCE_ERR_INVALID_ARG, FLCE_ERR_ALIGN, FLCE_ERR_WORKSPACE, FLCE_ERR_HIP 
 FLCE_F32, FLCE_BF16, FLCE_F16 = 0, 1, 2
 FLCE_STATIC_SCRATCH_BYTES = 144 << 20  # include/flce.h
 # enum flce_kernel_id of include/flce.h
-KERNEL_NAMES = ["fwd", "fwd_keep", "fwd_combine", "fwd_finalize", "bwd_prep", "dz", "dh", "dh_acc", "dh_final",
-                "dh_acc_final", "dw", "dw_acc", "labels", "keep_to_dz", "dhdw"]
+KERNEL_NAMES = ["fwd", "fwd_keep", "fwd_combine", "fwd_finalize", "bwd_prep", "dz", "dhdw", "labels", "keep_to_dz"]
 IGNORE_INDEX = -100
 
 # symbol -> (restype, argtypes), in the order of include/flce.h, flce_ce.h, flce_norm.h

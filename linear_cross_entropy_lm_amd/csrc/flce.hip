@@ -1572,15 +1572,6 @@ __device__ __forceinline__ void dh_body(char* lds, const T* __restrict__ slab, i
   const int count = my_tile_count(tiles);
   if (count > 0) gemm_run<T>(lds, count, even_slices<T>(vc_act), mk, epi);
 }
-template <typename T, bool ACCUM, bool FINAL>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dh(const T* __restrict__ slab, int ld_slab,
-                                                       const T* __restrict__ W, int D, int v0c, int vc_act,
-                                                       int t0c, int tc_act, int n_tiles_d,
-                                                       float* __restrict__ dacc, T* __restrict__ dH,
-                                                       const float* __restrict__ oscale) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
-  dh_body<T, ACCUM, FINAL>(lds, slab, ld_slab, W, D, v0c, vc_act, t0c, tc_act, n_tiles_d, dacc, dH, oscale);
-}
 
 // dW rows of one vocab chunk (+)= slab^T x H[token chunk]; C[v][d].  Persistent over tiles
 // b = (vt, dt) in the order of tile_rc.
@@ -1608,14 +1599,6 @@ __device__ __forceinline__ void dw_body(char* lds, const T* __restrict__ slab, i
   };
   const int count = my_tile_count(tiles);
   if (count > 0) gemm_run<T>(lds, count, even_slices<T>(tc_act), mk, epi);
-}
-template <typename T, bool ACCUM>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dw(const T* __restrict__ slab, int ld_slab,
-                                                       const T* __restrict__ H, int D, int t0c, int tc_act,
-                                                       int v0c, int vc_act, int n_tiles_d, float* __restrict__ dW,
-                                                       const float* __restrict__ oscale) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
-  dw_body<T, ACCUM>(lds, slab, ld_slab, H, D, t0c, tc_act, v0c, vc_act, n_tiles_d, dW, oscale);
 }
 
 // dH and dW of one (token chunk, vocabulary chunk) in one launch: both contract the same dz
@@ -1816,6 +1799,17 @@ void launch(int id, void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t s, 
   kernel<<<grid, block, 0, s>>>(args...);
 }
 
+// The eight variants of bwd_dhdw, indexed by (dH adds to an earlier vocabulary chunk's
+// partial) + 2 (dH is converted to the output type) + 4 (dW adds to an earlier token chunk's).
+template <typename T> const auto& dhdw_kernels() {
+  using K = void (*)(const T*, int, const T*, const T*, int, int, int, int, int, int, float*, T*, float*, const float*);
+  static constexpr K k[8] = {bwd_dhdw<T, false, false, false>, bwd_dhdw<T, true, false, false>,
+                             bwd_dhdw<T, false, true, false>,  bwd_dhdw<T, true, true, false>,
+                             bwd_dhdw<T, false, false, true>,  bwd_dhdw<T, true, false, true>,
+                             bwd_dhdw<T, false, true, true>,   bwd_dhdw<T, true, true, true>};
+  return k;
+}
+
 template <typename T>
 flce_status forward_impl(const T* H, const T* W, const int64_t* y, int N, int D, int V, int64_t ignore_index,
                          float* loss, float* lse, int32_t* n_valid, int32_t* dev_status, char* ws,
@@ -1862,14 +1856,6 @@ flce_status backward_impl(const T* H, const T* W, const int64_t* y, const float*
   const int64_t t_tiles = ceil_div(N, kTile), v_tiles = ceil_div(V, kTile);
   auto grid = [](int tiles) { return (unsigned)(tiles < kPersistentWGs ? tiles : kPersistentWGs); };
   T* slab = reinterpret_cast<T*>(ws + L.slab);
-  // bwd_dhdw's variant: whether dH adds to an earlier vocabulary chunk's partial, converts it
-  // to the output type, and whether dW adds to an earlier token chunk's.
-  using DhDw = void (*)(const T*, int, const T*, const T*, int, int, int, int, int, int, float*, T*, float*,
-                        const float*);
-  static constexpr DhDw kDhDw[8] = {bwd_dhdw<T, false, false, false>, bwd_dhdw<T, true, false, false>,
-                                    bwd_dhdw<T, false, true, false>,  bwd_dhdw<T, true, true, false>,
-                                    bwd_dhdw<T, false, false, true>,  bwd_dhdw<T, true, false, true>,
-                                    bwd_dhdw<T, false, true, true>,   bwd_dhdw<T, true, true, true>};
   for (int ci = 0; ci < n_tc; ++ci) {
     const int t0c = (int)(ci * t_tiles / n_tc * kTile);
     const int t1c = (int)((ci + 1) * t_tiles / n_tc * kTile);
@@ -1890,8 +1876,8 @@ flce_status backward_impl(const T* H, const T* W, const int64_t* y, const float*
                tc_act, n_tt, e2, coef, lab, slab, ld_slab);
       const bool acc_dh = vi > 0, fin = dacc && vi == n_vc - 1, acc_dw = ci > 0;
       const int tiles = n_tt > n_vt ? n_tt * n_td : n_vt * n_td;
-      launch(FLCE_KERNEL_DHDW, kDhDw[(acc_dh ? 1 : 0) + (fin ? 2 : 0) + (acc_dw ? 4 : 0)], dim3(grid(tiles)),
-             dim3(kThreads), s, slab, ld_slab, W, H, D, v0c, vc_act, t0c, tc_act, n_td, acc_rows, dH, dW, oscale);
+      launch(FLCE_KERNEL_DHDW, dhdw_kernels<T>()[(acc_dh ? 1 : 0) + (fin ? 2 : 0) + (acc_dw ? 4 : 0)],
+             dim3(grid(tiles)), dim3(kThreads), s, slab, ld_slab, W, H, D, v0c, vc_act, t0c, tc_act, n_td, acc_rows, dH, dW, oscale);
     }
   }
   return launched();
@@ -1948,19 +1934,14 @@ flce_status single_pass_impl(const T* H, const T* W, const int64_t* y, const flo
     const int64_t pieces = (int64_t)rows * P;
     launch(FLCE_KERNEL_KEEP_TO_DZ, keep_to_dz<T>, dim3((unsigned)(pieces < (1 << 20) ? pieces : (1 << 20))), dim3(kDzThreads), s,
         keep, ld, rows, mkeep, ld_m, e2, coef, lab, pieces, P);
+    // dH of the chunk over the whole vocabulary (K = V: no partial to carry) and its dW share,
+    // in one launch; fp32 writes dH directly, 16-bit types convert it on the way out.
     const int n_tt = ntn, n_vt = (int)ceil_div(V, kTile);
-    if (dtype == FLCE_F32)
-      launch(FLCE_KERNEL_DH, bwd_dh<T, false, false>, dim3(grid((int64_t)n_tt * n_td)), dim3(kThreads), s,
-          keep, ld, W, D, 0, V, t0, rows, n_td, reinterpret_cast<float*>(dH) + (int64_t)t0 * D, dH, oscale);
-    else
-      launch(FLCE_KERNEL_DH_FINAL, bwd_dh<T, false, true>, dim3(grid((int64_t)n_tt * n_td)), dim3(kThreads), s,
-          keep, ld, W, D, 0, V, t0, rows, n_td, reinterpret_cast<float*>(ws), dH, oscale);
-    if (ci > 0)
-      launch(FLCE_KERNEL_DW_ACC, bwd_dw<T, true>, dim3(grid((int64_t)n_vt * n_td)), dim3(kThreads), s, keep, ld, H, D, t0, rows, 0, V,
-                                                                                  n_td, dW, oscale);
-    else
-      launch(FLCE_KERNEL_DW, bwd_dw<T, false>, dim3(grid((int64_t)n_vt * n_td)), dim3(kThreads), s, keep, ld, H, D, t0, rows, 0, V,
-                                                                                   n_td, dW, oscale);
+    const int tiles = (n_tt > n_vt ? n_tt : n_vt) * n_td;
+    float* dh_rows = dtype == FLCE_F32 ? reinterpret_cast<float*>(dH) + (int64_t)t0 * D : nullptr;
+    const int variant = (dtype == FLCE_F32 ? 0 : 2) + (ci > 0 ? 4 : 0);
+    launch(FLCE_KERNEL_DHDW, dhdw_kernels<T>()[variant], dim3(grid(tiles)), dim3(kThreads), s, keep, ld, W, H, D, 0,
+           V, t0, rows, n_td, dh_rows, dH, dW, oscale);
   }
   launch(FLCE_KERNEL_FWD_FINALIZE, fwd_finalize, dim3(1), dim3(256), s, bloss, bcnt, bbad, L.nblk, loss, n_valid, dev_status);
   return launched();

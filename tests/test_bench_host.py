@@ -38,8 +38,8 @@ def _write_counters(path, kernel, counter, values, tag="x"):
         w.writerow([99, "other_kernel", counter, 1e9])
 
 
-@pytest.mark.parametrize("path,kinds", [("fused", ["fwd_tiles16", "bwd_dz16", "bwd_dh", "bwd_dw"]),
-                                        ("single", ["fwd_tiles16_keep", "bwd_dw"]), ("ce", ["ce_rows_bwd"]),
+@pytest.mark.parametrize("path,kinds", [("fused", ["fwd_tiles16", "bwd_dz16", "bwd_dhdw"]),
+                                        ("single", ["fwd_tiles16_keep", "bwd_dhdw"]), ("ce", ["ce_rows_bwd"]),
                                         ("norm", ["rms_bwd"])])
 def test_summarize_counters_scales_by_the_copy(tmp_path, monkeypatch, path, kinds):
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
@@ -48,8 +48,7 @@ def test_summarize_counters_scales_by_the_copy(tmp_path, monkeypatch, path, kind
     names = {"fwd_tiles16": "(anonymous namespace)::fwd_tiles16<unsigned short, false>",
              "fwd_tiles16_keep": "(anonymous namespace)::fwd_tiles16<unsigned short, true>",
              "bwd_dz16": "(anonymous namespace)::bwd_dz16<unsigned short>",
-             "bwd_dh": "(anonymous namespace)::bwd_dh<unsigned short, true, false>",
-             "bwd_dw": "(anonymous namespace)::bwd_dw<unsigned short, true>",
+             "bwd_dhdw": "(anonymous namespace)::bwd_dhdw<unsigned short, true, false, true>",
              "ce_rows_bwd": "(anonymous namespace)::ce_rows_bwd<1>", "rms_bwd": "(anonymous namespace)::rms_bwd<1, 2>"}
     for i, kind in enumerate(kinds):
         _write_counters(root / "F", names[kind], "FETCH_SIZE", [1000.0 * (i + 1), 3000.0 * (i + 1)], f"k{i}")
@@ -78,9 +77,9 @@ def test_kernel_patterns_tell_the_forward_variants_apart():
 
 def test_traffic_record_of_another_source_is_ignored(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
-    with open(bench.traffic_path("bwd_dw", "llama3"), "w") as f:
+    with open(bench.traffic_path("bwd_dhdw", "llama3"), "w") as f:
         f.write(json.dumps({"source_digest": "0" * 16, "workload": "llama3", "hbm_bytes_per_launch": 1.0}))
-    assert bench.load_traffic("bwd_dw", "llama3") is None
+    assert bench.load_traffic("bwd_dhdw", "llama3") is None
 
 
 def test_chunk_spans_partition_whole_tiles():
@@ -93,23 +92,22 @@ def test_chunk_spans_partition_whole_tiles():
     assert bench.chunk_spans(128256, 8192)[0] == (0, 7936)  # 501 tiles over 16 chunks: 31 or 32 tiles
 
 
-@pytest.mark.parametrize("path,tc,vc,mode", [("fused", 4096, 8192, "separate"), ("fused", 4096, 8192, "dhdw"),
-                                              ("single", 4096, 0, None), ("single", 8192, 0, None)])
-def test_gemm_launch_flops_cover_the_work_once(path, tc, vc, mode):
-    """The GEMM launches of a step add up to the forward (2 N V D, or none for a single
-    pass's separate kinds) plus three 2 N V D contractions of the backward."""
+@pytest.mark.parametrize("path,tc,vc", [("fused", 4096, 8192), ("single", 4096, 0), ("single", 8192, 0)])
+def test_gemm_launch_flops_cover_the_work_once(path, tc, vc):
+    """The GEMM launches of a step add up to the forward (2 N V D; the single pass's keep
+    forward) and the backward's contractions (two of 2 N V D for dH and dW, and the dz
+    recompute's 2 N V D on the recomputing path)."""
     N, D, V = 16384, 4096, 128256
-    kw = {} if mode is None else dict(separate=mode == "separate")
-    launches = bench.gemm_launch_flops(path, N, D, V, tc, vc, **kw)
+    launches = bench.gemm_launch_flops(path, N, D, V, tc, vc)
     assert sum(f for _, f in launches) == pytest.approx((4.0 if path == "fused" else 3.0) * 2.0 * N * V * D)
-    if mode == "separate":
-        assert len(launches) == 1 + 3 * 4 * 16
-        assert [k for k, _ in launches[1:4]] == [5, 6, 10] and [k for k, _ in launches[-3:]] == [5, 9, 11]
-    elif mode == "dhdw":
-        assert [k for k, _ in launches] == [0] + [5, 14] * 64
-        assert launches[2][1] == pytest.approx(2 * launches[1][1])
+    for kind in bench.GEMM_KINDS[path]["f16"]:
+        ids = set(bench.KINDS[kind][1])
+        contractions = 2 if kind == "bwd_dhdw" else 1
+        assert sum(f for k, f in launches if k in ids) == pytest.approx(contractions * 2.0 * N * V * D)
+    if path == "fused":
+        assert [k for k, _ in launches] == [0] + [5, 6] * 64
     else:
-        assert len(launches) == 3 * (N // tc)
+        assert [k for k, _ in launches] == [1, 6] * (N // tc)
 
 
 def test_more_than_one_gpu_is_refused(capsys, monkeypatch):
@@ -178,8 +176,8 @@ def test_sclk_sampler_reads_the_current_level(tmp_path):
 def test_traffic_record_of_another_workload_is_ignored(tmp_path, monkeypatch):
     """A record taken on the Llama-3 workload does not describe a run on another one."""
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
-    with open(bench.traffic_path("bwd_dh", "llama3"), "w") as f:
+    with open(bench.traffic_path("bwd_dhdw", "llama3"), "w") as f:
         f.write(json.dumps({"source_digest": bench.source_digest("fused"), "workload": "llama3",
                             "hbm_bytes_per_launch": 5.0}))
-    assert bench.load_traffic("bwd_dh", "llama3") == 5.0
-    assert bench.load_traffic("bwd_dh", "llama2") is None
+    assert bench.load_traffic("bwd_dhdw", "llama3") == 5.0
+    assert bench.load_traffic("bwd_dhdw", "llama2") is None
