@@ -78,8 +78,14 @@ KINDS = {
 TRAFFIC_RECORD = {"fwd_tiles16": "fwd_tiles", "fwd_tiles16_keep": "fwd_tiles_keep"}
 
 
-def traffic_path(kind: str, workload: str) -> str:
-    return os.path.join(PROFILES, f"{TRAFFIC_RECORD.get(kind, kind)}_{workload}_traffic.json")
+def traffic_path(kind: str, workload: str, path: str = "fused") -> str:
+    """The counter record of kernel `kind` on `workload` under schedule `path`.  A kind that
+    both schedules launch (the dH + dW launch) runs other chunk shapes in the single pass,
+    so that path's record carries its own name."""
+    base = TRAFFIC_RECORD.get(kind, kind)
+    if path == "single" and kind in GEMM_KINDS["fused"]["f16"]:
+        base += "_single"
+    return os.path.join(PROFILES, f"{base}_{workload}_traffic.json")
 
 
 def code_digest(text: str) -> str:
@@ -99,13 +105,15 @@ def source_digest(path: str = "fused") -> str:
 
 def load_traffic(kind: str, workload: str, path: str = "fused"):
     """HBM bytes per launch of kernel `kind` on `workload` from its committed counter record,
-    or None when absent, taken on a different kernel source, or on another workload."""
+    or None when absent, taken on a different kernel source, on another workload or under
+    another schedule."""
     try:
-        with open(traffic_path(kind, workload)) as f:
+        with open(traffic_path(kind, workload, path)) as f:
             t = json.load(f)
     except OSError:
         return None
-    if t.get("source_digest") != source_digest(path) or t.get("workload") != workload:
+    if (t.get("source_digest") != source_digest(path) or t.get("workload") != workload
+            or t.get("path", path) != path):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -160,13 +168,13 @@ def summarize_counters(root: str, copy_bytes: int, path: str, kinds: list[str], 
         pattern = KINDS[kind][0]
         fetch, n_f = _counter_per_dispatch(os.path.join(root, "F"), "FETCH_SIZE", pattern)
         write, n_w = _counter_per_dispatch(os.path.join(root, "W"), "WRITE_SIZE", pattern)
-        rec = {"kernel": kind, "kernel_name_pattern": pattern, "workload": workload,
+        rec = {"kernel": kind, "kernel_name_pattern": pattern, "workload": workload, "path": path,
                "source_digest": source_digest(path),
                "fetch_kib_per_launch": fetch, "write_kib_per_launch": write, "launches": [n_f, n_w],
                "copy_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
                "fetch_factor": f_factor, "write_factor": w_factor,
                "hbm_bytes_per_launch": fetch * 1024.0 * f_factor + write * 1024.0 * w_factor}
-        with open(traffic_path(kind, workload), "w") as f:
+        with open(traffic_path(kind, workload, path), "w") as f:
             json.dump(rec, f, indent=1)
             f.write("\n")
         out.append(rec)

@@ -43,15 +43,19 @@
 //   bwd_dz16 / bwd_dz
 //                 recompute a Z^T tile of one (vocab chunk, token chunk), form
 //                 dz = (p - onehot) * g/N_valid, write it to the chunk slab.
-//   bwd_dh        dH[chunk rows] (+)= slab x W[vocab chunk]   (fp32 accumulator)
-//   bwd_dw        dW[vocab chunk] (+)= slab^T x H[token chunk]
+//   bwd_dhdw      both contractions of one chunk in one launch: each workgroup runs its
+//                 dH tiles, dH[chunk rows] (+)= slab x W[vocab chunk] (fp32 accumulator),
+//                 and its dW tiles, dW[vocab chunk] (+)= slab^T x H[token chunk]; odd
+//                 workgroups take the dW tiles first, so the two fp32 read-modify-write
+//                 epilogues do not fall on every CU at the same moment.
 // Single pass (flce_forward_backward with its larger workspace), per token chunk:
 //   label_blocks, label_total   N_valid of the whole call before any chunk's backward.
 //   fwd_tiles16<KEEP> / fwd_tiles<KEEP> the forward tiles, which also keep p~ = exp(z - m) (m the maximum over
 //                 a half tile of 128 vocabulary rows) in the input type, and m.
 //   fwd_combine, bwd_prep       as above, for the chunk's rows.
 //   keep_to_dz    p~ -> dz in place once lse is known (HBM-bound pass over the slab).
-//   bwd_dh        dH of the chunk with K = V in one launch; bwd_dw accumulates dW.
+//   bwd_dhdw      dH of the chunk with K = V (no accumulator) and dW accumulated over
+//                 the chunks, in one launch.
 // Backward runs token chunks outer, vocabulary chunks inner; each output tile has one
 // owner per launch and chunks are visited in a fixed order, so dW's split over tokens
 // (and dH's over vocabulary) is deterministic without atomics.
@@ -816,7 +820,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles(const T* __restrict__ H
 // MFMA draws less power per flop (MFMAs alone: 84% of the dense peak at 2.05 GHz against
 // 70-74% at 1.6-1.8 GHz for 32 x 32 x 16), so these kernels run at a higher clock; it
 // needs a leaner register schedule than the other core (below) to fit two waves per SIMD.
-// bwd_dh and bwd_dw stay on the 32 x 32 core: with their transposed operands (two
+// The dH and dW contractions stay on the 32 x 32 core: with their transposed operands (two
 // transposing reads per fragment) this core measured slower, stalled on those reads
 // behind products half as long, below the power limit.
 // ---------------------------------------------------------------------------------

@@ -165,10 +165,10 @@ inline void chunk_span(int64_t total, int64_t chunk, int64_t i, int64_t* first, 
 // Every operand of the backward's launches for chunks of tc x vc (the largest chunk of
 // each kind):
 //   bwd_dz: W and H as 256-row K-contiguous tiles of D elements;
-//   bwd_dh: the slab (rows at a pitch of vc elements, K = the vocabulary chunk) and W
-//           (MN-contiguous over the chunk's vc rows at a pitch of D);
-//   bwd_dw: the slab (MN-contiguous over tc token rows at a pitch of vc) and H
-//           (MN-contiguous over tc rows at a pitch of D);
+//   bwd_dhdw, dH tiles: the slab (rows at a pitch of vc elements, K = the vocabulary
+//           chunk) and W (MN-contiguous over the chunk's vc rows at a pitch of D);
+//   bwd_dhdw, dW tiles: the slab (MN-contiguous over tc token rows at a pitch of vc) and
+//           H (MN-contiguous over tc rows at a pitch of D);
 // and the tile counts of each launch.
 inline bool bwd_ranges_ok(int64_t D, int dtype, int64_t tc, int64_t vc) {
   const size_t es = elem_size(dtype);
@@ -268,10 +268,10 @@ inline SpLayout sp_layout(int64_t N, int64_t V, int dtype, int64_t tc) {
 
 // Operands of the single pass's launches for a token chunk of tc rows:
 //   fwd_tiles<KEEP>: W and H as 256-row K-contiguous tiles of D elements;
-//   bwd_dh: the kept slab (rows at a pitch of ld, K = the whole vocabulary) and W
-//           (MN-contiguous over all V rows at a pitch of D);
-//   bwd_dw: the kept slab (MN-contiguous over tc rows at a pitch of ld) and H
-//           (MN-contiguous over tc rows at a pitch of D);
+//   bwd_dhdw, dH tiles: the kept slab (rows at a pitch of ld, K = the whole vocabulary)
+//           and W (MN-contiguous over all V rows at a pitch of D);
+//   bwd_dhdw, dW tiles: the kept slab (MN-contiguous over tc rows at a pitch of ld) and
+//           H (MN-contiguous over tc rows at a pitch of D);
 // the tile counts of each launch, and keep_to_dz's 16-byte chunks per row.
 inline bool sp_ranges_ok(int64_t D, int64_t V, int dtype, int64_t tc) {
   const size_t es = elem_size(dtype);

@@ -61,7 +61,7 @@ def test_summarize_counters_scales_by_the_copy(tmp_path, monkeypatch, path, kind
         assert rec["fetch_kib_per_launch"] == 2000.0 * (i + 1) and rec["write_kib_per_launch"] == 500.0
         assert rec["fetch_factor"] == pytest.approx(2.0) and rec["write_factor"] == pytest.approx(1.0)
         assert rec["hbm_bytes_per_launch"] == pytest.approx(2000.0 * (i + 1) * 1024 * 2 + 500.0 * 1024)
-        saved = json.loads(open(bench.traffic_path(kind, "w")).read())
+        saved = json.loads(open(bench.traffic_path(kind, "w", path)).read())
         assert saved["source_digest"] == bench.source_digest(path)
         assert bench.load_traffic(kind, "w", path) == pytest.approx(rec["hbm_bytes_per_launch"])
 
@@ -80,6 +80,22 @@ def test_traffic_record_of_another_source_is_ignored(tmp_path, monkeypatch):
     with open(bench.traffic_path("bwd_dhdw", "llama3"), "w") as f:
         f.write(json.dumps({"source_digest": "0" * 16, "workload": "llama3", "hbm_bytes_per_launch": 1.0}))
     assert bench.load_traffic("bwd_dhdw", "llama3") is None
+
+
+def test_single_pass_record_does_not_shadow_the_default_one(tmp_path, monkeypatch):
+    """The dH + dW launch runs in both schedules at other chunk shapes: each schedule's
+    record has its own file and is only read back under that schedule."""
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    assert bench.traffic_path("bwd_dhdw", "llama3", "single") != bench.traffic_path("bwd_dhdw", "llama3", "fused")
+    for path, value in (("fused", 1.0), ("single", 20.0)):
+        with open(bench.traffic_path("bwd_dhdw", "llama3", path), "w") as f:
+            f.write(json.dumps({"source_digest": bench.source_digest(path), "workload": "llama3", "path": path,
+                                "hbm_bytes_per_launch": value}))
+    assert bench.load_traffic("bwd_dhdw", "llama3", "fused") == 1.0
+    assert bench.load_traffic("bwd_dhdw", "llama3", "single") == 20.0
+    # a record written under one schedule and copied to the other's name is refused
+    os.replace(bench.traffic_path("bwd_dhdw", "llama3", "fused"), bench.traffic_path("bwd_dhdw", "llama3", "single"))
+    assert bench.load_traffic("bwd_dhdw", "llama3", "single") is None
 
 
 def test_chunk_spans_partition_whole_tiles():
