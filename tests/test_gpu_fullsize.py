@@ -66,13 +66,22 @@ def test_fullsize_parity(name):
     assert bool(torch.isfinite(dH).all()) and bool(torch.isfinite(dW).all())
     ignored = y == -100
     assert bool((dH[ignored] == 0).all())
+    # Every dz row sums to zero before rounding, so dW's columns sum to zero up to the
+    # rounding of dz to the input type.  The label element -c (1 - p) dominates each row and
+    # rounds the same way in almost every row, so the residual is that element's relative
+    # rounding error, at most half an ulp: 2^-8 in bf16, 2^-11 in fp16 (measured 2.0e-3 and
+    # 7e-5 at most over these workloads).  The bound is that half ulp with a 1.3x margin.
     colsum = dW.double().sum(dim=0).norm().item()
-    assert colsum <= 1e-2 * dW.double().norm().item()
+    col_tol = 5e-3 if cfg.dtype == "bf16" else 6.5e-4
+    assert colsum <= col_tol * dW.double().norm().item()
+    # <dW, W> = <dz, H W^T> = <dH, H> holds exactly for the rounded dz both products share;
+    # what is left is fp32 accumulation order and the rounding of dH to the input type
+    # (measured 2.2e-5 at most).
     lhs = (dW.double() * W.double()).sum().item()
     rhs = (dH.double() * H.double()).sum().item()
     print(f"|1^T dW| / |dW| {colsum / dW.double().norm().item():.2e}; <dW,W> vs <dH,H> rel "
           f"{abs(lhs - rhs) / abs(lhs):.2e}", flush=True)
-    assert abs(lhs - rhs) <= 1e-2 * abs(lhs)
+    assert abs(lhs - rhs) <= 5e-4 * abs(lhs)
     if name == "llama3":
         assert scratch_fraction(ws_bytes, N, V) <= 0.05
 
