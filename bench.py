@@ -50,6 +50,17 @@ METRIC = "fused linear-CE fwd+bwd tokens/s at N=16384,D=4096,V=128256; % bf16 MF
 METRIC_CE = "cross-entropy over materialised logits fwd+bwd tokens/s at N=16384,V=128256; % HBM peak"
 METRIC_NORM = "RMSNorm fwd+fused bwd tokens/s at N=16384,D=4096; % HBM peak"
 METRIC_SINGLE = "fused linear-CE fwd+bwd in one call, single pass, tokens/s at N=16384,D=4096,V=128256; % bf16 MFMA peak"
+
+
+def workload_metric(metric: str, cfg) -> str:
+    """The metric's text with the sizes of the workload actually run (the headline string
+    for the Llama-3-shaped bf16 head it is quoted on; fp16 runs say so)."""
+    import re
+    sizes = ",".join(f"{k}={getattr(cfg, k)}" for k in ("N", "D", "V") if f"{k}=" in metric and hasattr(cfg, k))
+    out = re.sub(r"at [NDV]=\d+(,[NDV]=\d+)*", f"at {sizes}", metric) if sizes else metric
+    if getattr(cfg, "dtype", "bf16") == "f16":
+        out = out.replace("% bf16 MFMA peak", "% fp16 MFMA peak")
+    return out
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "linear_cross_entropy_lm_amd", "csrc")
@@ -406,7 +417,7 @@ def run_fused(args) -> dict:
     timing = None if args.no_kernel_timing else time_launches(args, B, step, stream, "fused", cfg, tc, vc)
 
     flop_step = 8.0 * N * V * D
-    out = _common(args, METRIC, N / (ms * 1e-3), ms, cfg.dtype,
+    out = _common(args, workload_metric(METRIC, cfg), N / (ms * 1e-3), ms, cfg.dtype,
                   "synthetic: seeded Gaussian H with unit-RMS rows, W ~ N(0, 0.02^2), uniform labels, "
                   f"{cfg.n_ignored} ignore_index rows",
                   {"workload": f"{cfg.name}-shaped lm_head + cross-entropy, fwd+bwd", "N": N, "D": D,
@@ -472,7 +483,7 @@ def run_single(args) -> dict:
         raise RuntimeError("the workspace does not buy the single-pass schedule")
     timing = None if args.no_kernel_timing else time_launches(args, B, step, stream, "single", cfg, tc, 0)
     flop_credit = 8.0 * N * V * D
-    out = _common(args, METRIC_SINGLE, N / (ms * 1e-3), ms, cfg.dtype,
+    out = _common(args, workload_metric(METRIC_SINGLE, cfg), N / (ms * 1e-3), ms, cfg.dtype,
                   "synthetic: seeded Gaussian H with unit-RMS rows, W ~ N(0, 0.02^2), uniform labels, "
                   f"{cfg.n_ignored} ignore_index rows",
                   {"workload": f"{cfg.name}-shaped lm_head + cross-entropy, fwd+bwd in one call (single pass)",
@@ -535,7 +546,7 @@ def run_ce(args) -> dict:
     fwd_row, bwd_row = ce_row_bytes(V, es)
     achieved = bwd_row * N / (bwd_ms * 1e-3) / 1e9
     step_bytes = (fwd_row + bwd_row) * N
-    out = _common(args, METRIC_CE, N / (ms * 1e-3), ms, cfg.dtype,
+    out = _common(args, workload_metric(METRIC_CE, cfg), N / (ms * 1e-3), ms, cfg.dtype,
                   f"synthetic: seeded logits N(0, {cfg.z_std}^2), uniform labels, {cfg.n_ignored} ignore_index rows",
                   {"workload": f"{cfg.name}: cross-entropy over materialised logits, fwd+bwd", "N": N, "V": V,
                    "row_pitch": cfg.pitch, "parallelism": "single GPU"})
@@ -608,7 +619,7 @@ def run_norm(args) -> dict:
     bwd_ms = ms - fwd_ms
     fwd_b, bwd_b = norm_bytes(N, D, es, min(N, 512))
     achieved = bwd_b / (bwd_ms * 1e-3) / 1e9
-    out = _common(args, METRIC_NORM, N / (ms * 1e-3), ms, cfg.dtype,
+    out = _common(args, workload_metric(METRIC_NORM, cfg), N / (ms * 1e-3), ms, cfg.dtype,
                   f"synthetic: seeded X ~ N(0, {cfg.x_std}^2), gamma ~ 1 + N(0, {cfg.gamma_std}^2), "
                   f"dH ~ N(0, {cfg.dh_std}^2), eps {cfg.eps:g}",
                   {"workload": f"{cfg.name}: RMSNorm of the hidden states before the lm_head, fwd + fused bwd",

@@ -197,3 +197,14 @@ def test_traffic_record_of_another_workload_is_ignored(tmp_path, monkeypatch):
                             "hbm_bytes_per_launch": 5.0}))
     assert bench.load_traffic("bwd_dhdw", "llama3") == 5.0
     assert bench.load_traffic("bwd_dhdw", "llama2") is None
+
+
+def test_metric_names_the_sizes_that_ran():
+    """The headline workload keeps the headline metric text; any other reports its own sizes."""
+    from linear_cross_entropy_lm_amd import inputs as I
+    assert bench.workload_metric(bench.METRIC, I.CONFIGS["llama3"]) == bench.METRIC
+    m = bench.workload_metric(bench.METRIC, I.CONFIGS["llama2"])
+    assert "N=4096,D=4096,V=32000" in m and "16384" not in m
+    assert "fp16 MFMA peak" in bench.workload_metric(bench.METRIC_SINGLE, I.CONFIGS["llama3_f16"])
+    assert bench.workload_metric(bench.METRIC_CE, I.LOGIT_CONFIGS["ce_llama3"]) == bench.METRIC_CE
+    assert bench.workload_metric(bench.METRIC_NORM, I.NORM_CONFIGS["norm_llama3"]) == bench.METRIC_NORM
