@@ -51,6 +51,10 @@ CASES = [
     ("D8_f32", I.case(257, 8, 1031, "f32", seed=23)),
     ("D8200_bf16", I.case(300, 8200, 1031, "bf16", seed=24)),
     ("D8200_f16", I.case(300, 8200, 1031, "f16", seed=25)),
+    # the widest rows the boundary accepts (D = 65536: a 256-row operand tile spans 32 or 64
+    # MiB of HBM, and the transposed operands' K rows are 128 or 256 KiB apart)
+    ("D65536_bf16", I.case(300, 65536, 1031, "bf16", seed=26)),
+    ("D65536_f32", I.case(300, 65536, 1031, "f32", seed=27)),
 ]
 
 
