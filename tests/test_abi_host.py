@@ -324,3 +324,22 @@ def test_static_rejects_before_touching_the_device(B):
     assert _fbs(B, dt=9) == B.FLCE_ERR_INVALID_ARG
     assert _fbs(B, H=None) == B.FLCE_ERR_INVALID_ARG
     assert _fbs(B, dW=None) == B.FLCE_ERR_INVALID_ARG
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """A copy of the package without libflce.so: importing the binding raises ImportError
+    (there is no CPU or torch fallback for any entry point)."""
+    import shutil
+    import subprocess
+    import sys
+    src = os.path.join(ROOT, "linear_cross_entropy_lm_amd")
+    dst = tmp_path / "linear_cross_entropy_lm_amd"
+    dst.mkdir()
+    for f in os.listdir(src):
+        if f.endswith(".py"):
+            shutil.copy(os.path.join(src, f), dst / f)
+    assert not (dst / "libflce.so").exists()
+    r = subprocess.run([sys.executable, "-c", "import linear_cross_entropy_lm_amd.binding"], cwd=tmp_path,
+                       env={**os.environ, "PYTHONPATH": str(tmp_path)}, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "libflce.so is missing" in r.stderr
