@@ -180,6 +180,57 @@ def test_bitwise_deterministic():
         assert np.array_equal(a[k], b[k]), k
 
 
+def test_two_streams_with_their_own_workspaces():
+    """Calls on two streams at once, each with its own workspace and outputs, give the same
+    bits as the same calls one after the other: the library keeps no state between calls
+    (the workloads differ in shape, so their launches overlap on the device)."""
+    from linear_cross_entropy_lm_amd import binding as B
+    dev = "cuda:0"
+    cfgs = [I.case(4500, 512, 9000, "bf16", seed=49), I.case(700, 384, 3000, "f16", seed=50)]
+    jobs = []
+    for cfg in cfgs:
+        inp = I.generate(cfg)
+        H, W, y = inp.device_tensors(dev)
+        N, D, V = cfg.N, cfg.D, cfg.V
+        jobs.append((H, W, y, N, D, V))
+
+    def outputs(job):
+        H, W, y, N, D, V = job
+        return dict(ws=torch.empty(B.flce_workspace_bytes(N, D, V, H.dtype), dtype=torch.uint8, device=dev),
+                    loss=torch.empty(1, dtype=torch.float32, device=dev),
+                    lse=torch.empty(N, dtype=torch.float32, device=dev),
+                    nv=torch.empty(1, dtype=torch.int32, device=dev), st=torch.empty(1, dtype=torch.int32, device=dev),
+                    dH=torch.full_like(H, float("nan")),
+                    dW=torch.full((V, D), float("nan"), dtype=torch.float32, device=dev))
+
+    def run(job, o, reps=3):
+        H, W, y = job[:3]
+        g = torch.tensor([1024.0 if H.dtype == torch.float16 else 1.0], dtype=torch.float32, device=dev)
+        for _ in range(reps):
+            B.flce_forward(H, W, y, o["loss"], o["lse"], o["nv"], o["st"], o["ws"])
+            B.flce_backward(H, W, y, o["lse"], o["nv"], g, o["dH"], o["dW"], o["ws"])
+
+    seq = [outputs(j) for j in jobs]
+    for j, o in zip(jobs, seq):
+        run(j, o)
+    torch.cuda.synchronize()
+    par = [outputs(j) for j in jobs]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for j, o, s in zip(jobs, par, streams):
+        with torch.cuda.stream(s):
+            run(j, o)
+    torch.cuda.synchronize()
+    for a, b in zip(seq, par):
+        assert int(a["st"].item()) == 0 and int(b["st"].item()) == 0
+        for k in ("loss", "lse", "nv", "dH", "dW"):
+            x, z = a[k], b[k]
+            if x.dtype.is_floating_point:
+                x = x.view(torch.int16 if x.element_size() == 2 else torch.int32)
+                z = z.view(torch.int16 if z.element_size() == 2 else torch.int32)
+            assert torch.equal(x, z), k
+
+
 def test_chunking_changes_only_rounding():
     from linear_cross_entropy_lm_amd import binding as B
     cfg = I.case(700, 384, 3000, "bf16", seed=47)
