@@ -41,6 +41,10 @@
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default stream).
  *    The return value reports only argument and launch errors.  Two calls may run
  *    concurrently only with distinct workspaces and outputs.
+ *  - A call issues kernel launches only (no allocation, memset, copy or synchronisation),
+ *    so it may be captured into a HIP graph and replayed; flce_forward_backward_static
+ *    looks up its array's device address on its first call on a device, so make one call
+ *    outside the capture first.
  *  - Results are deterministic: fixed tile shapes and fixed reduction orders, no
  *    floating-point atomics; a repeated call with the same inputs and the same
  *    workspace_bytes produces bitwise-identical outputs.

@@ -231,6 +231,59 @@ def test_two_streams_with_their_own_workspaces():
             assert torch.equal(x, z), k
 
 
+@pytest.mark.parametrize("entry", ["two_calls", "static"])
+def test_graph_capture_replays_match_eager(entry):
+    """The library launches kernels only (no allocation, memset, copy or synchronisation), so
+    its calls can be captured into a HIP graph.  The graph is replayed several times with
+    eager work and synchronisations in between, and every replay must give the eager bits."""
+    from linear_cross_entropy_lm_amd import binding as B
+    dev = "cuda:0"
+    cfg = I.case(2500, 512, 7000, "bf16", seed=51)
+    inp = I.generate(cfg)
+    H, W, y = inp.device_tensors(dev)
+    N, D, V = cfg.N, cfg.D, cfg.V
+    ws = torch.empty(B.flce_workspace_bytes(N, D, V, H.dtype), dtype=torch.uint8, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    nv = torch.empty(1, dtype=torch.int32, device=dev)
+    st = torch.empty(1, dtype=torch.int32, device=dev)
+    dH = torch.empty_like(H)
+    dW = torch.empty(V, D, dtype=torch.float32, device=dev)
+
+    def step():
+        if entry == "static":
+            B.flce_forward_backward_static(H, W, y, None, loss, lse, nv, st, dH, dW)
+        else:
+            B.flce_forward(H, W, y, loss, lse, nv, st, ws)
+            B.flce_backward(H, W, y, lse, nv, None, dH, dW, ws)
+
+    def snapshot():
+        return [t.clone() for t in (loss, lse, nv, st, dH, dW)]
+
+    step()  # eager (also resolves the static array's device address before capture)
+    torch.cuda.synchronize()
+    eager = snapshot()
+    assert int(eager[3].item()) == 0
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in (loss, lse, dH, dW):  # eager work between replays: outputs scribbled on
+            t.fill_(float("nan"))
+        nv.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(eager, snapshot()):
+            x, z = (a, b) if not a.dtype.is_floating_point else (
+                a.view(torch.int16 if a.element_size() == 2 else torch.int32),
+                b.view(torch.int16 if b.element_size() == 2 else torch.int32))
+            assert torch.equal(x, z), f"replay {rep}"
+
+
 def test_chunking_changes_only_rounding():
     from linear_cross_entropy_lm_amd import binding as B
     cfg = I.case(700, 384, 3000, "bf16", seed=47)
