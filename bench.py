@@ -854,6 +854,47 @@ def summarize_occupancy(csv_dir: str, min_us: float = 100.0) -> list[dict]:
     return out
 
 
+MOPS_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_F32")
+
+
+def summarize_mops(csv_dir: str, workload: str, path: str = "fused") -> list[dict]:
+    """Executed matrix-core flops, from one rocprofv3 --pmc run of MOPS_COUNTERS under
+    csv_dir (each counter counts multiplies and adds over 512, summed over the chip): one
+    record per kernel (dispatches, flops per dispatch), then one for the whole run per call
+    of the path (the calls are counted by fwd_finalize, launched once per forward or
+    one-call pass), set against the flops the path is credited with: 8 N V D for the
+    recomputing schedule (forward, dz recompute, dH, dW), 6 N V D for the single pass."""
+    import csv
+    import glob
+    import re
+
+    from linear_cross_entropy_lm_amd import inputs as I
+    disp = {}
+    for p in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] not in MOPS_COUNTERS:
+                    continue
+                d = disp.setdefault((p, r["Dispatch_Id"]), {"name": r["Kernel_Name"], "flop": 0.0})
+                d["flop"] += 512.0 * float(r["Counter_Value"])
+    per = {}
+    for d in disp.values():
+        name = re.sub(r"\(anonymous namespace\)::|void ", "", d["name"]).split("(")[0].strip()
+        a = per.setdefault(name, {"dispatches": 0, "flop": 0.0})
+        a["dispatches"] += 1
+        a["flop"] += d["flop"]
+    calls = sum(a["dispatches"] for n, a in per.items() if n.startswith("fwd_finalize"))
+    out = [{"kernel": n, "dispatches": a["dispatches"], "tflop_per_dispatch": a["flop"] / a["dispatches"] / 1e12}
+           for n, a in sorted(per.items(), key=lambda kv: -kv[1]["flop"]) if a["flop"] > 0]
+    cfg = I.CONFIGS[workload]
+    credited = (6 if path == "single" else 8) * cfg.N * cfg.V * cfg.D
+    total = sum(a["flop"] for a in per.values())
+    out.append({"workload": workload, "path": path, "calls": calls,
+                "executed_tflop_per_call": total / max(calls, 1) / 1e12, "credited_tflop_per_call": credited / 1e12,
+                "executed_over_credited": total / max(calls, 1) / credited})
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
@@ -883,6 +924,9 @@ def main() -> int:
     ap.add_argument("--summarize-occupancy", metavar="DIR",
                     help="only print, per kernel, clock, MFMA-busy and LDS figures from one rocprofv3 --pmc "
                          "run of bench.OCCUPANCY_COUNTERS under DIR; no GPU needed")
+    ap.add_argument("--summarize-mops", metavar="DIR",
+                    help="only print executed MFMA flops per kernel and per call, from one rocprofv3 --pmc run "
+                         "of bench.MOPS_COUNTERS under DIR (--path, --workload name the run); no GPU needed")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     ap.add_argument("--kinds", default=None,
                     help="--summarize-counters: comma-separated kernel kinds (default: the path's GEMMs)")
@@ -893,6 +937,10 @@ def main() -> int:
         return 0
     if args.summarize_occupancy:
         for rec in summarize_occupancy(args.summarize_occupancy):
+            print(json.dumps(rec), flush=True)
+        return 0
+    if args.summarize_mops:
+        for rec in summarize_mops(args.summarize_mops, args.workload or "llama3", args.path):
             print(json.dumps(rec), flush=True)
         return 0
     if args.summarize_counters:

@@ -8,6 +8,7 @@ import os
 import pytest
 
 import bench
+from linear_cross_entropy_lm_amd import inputs as I
 
 
 def test_ce_row_bytes():
@@ -166,6 +167,39 @@ def test_summarize_occupancy(tmp_path):
     assert r["mfma_busy"] == pytest.approx(0.5) and r["mfma_busy_ghz"] == pytest.approx(1.0)
     assert r["lds_active"] == pytest.approx(0.25) and r["lds_bank_conflict"] == pytest.approx(0.01)
     assert r["lds_issue_wait"] == pytest.approx(0.1)
+
+
+def test_summarize_mops(tmp_path):
+    """Two calls of the recomputing schedule at the tiny workload: per call a forward of
+    2 N V D, a dz recompute of 2 N V D and two dH + dW launches of 2 N V D each (flops over
+    512 in the counter, on two counters' rows), and one fwd_finalize: executed equals the
+    credited 8 N V D per call."""
+    cfg = I.CONFIGS["tiny_f32"]
+    unit = 2 * cfg.N * cfg.V * cfg.D
+    rows = []
+    for call in range(2):
+        rows += [("void (anonymous namespace)::fwd_tiles<float, false>(int)", unit),
+                 ("void (anonymous namespace)::bwd_dz<float>(int)", unit),
+                 ("void (anonymous namespace)::bwd_dhdw<float, false, false, false>(int)", unit),
+                 ("void (anonymous namespace)::bwd_dhdw<float, true, false, false>(int)", unit),
+                 ("void (anonymous namespace)::fwd_finalize(int)", 0)]
+    with open(tmp_path / "m_counter_collection.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for d, (name, flop) in enumerate(rows):
+            w.writerow([d, name, "SQ_INSTS_VALU_MFMA_MOPS_F32", flop / 512 * 0.75])
+            w.writerow([d, name, "SQ_INSTS_VALU_MFMA_MOPS_F32", flop / 512 * 0.25])
+            w.writerow([d, name, "SQ_INSTS_VALU_MFMA_MOPS_BF16", 0])
+            w.writerow([d, name, "GRBM_GUI_ACTIVE", 123456])
+    recs = bench.summarize_mops(str(tmp_path), "tiny_f32")
+    per = {r["kernel"]: r for r in recs[:-1]}
+    assert set(per) == {"fwd_tiles<float, false>", "bwd_dz<float>", "bwd_dhdw<float, false, false, false>",
+                        "bwd_dhdw<float, true, false, false>"}
+    assert all(r["dispatches"] == 2 and r["tflop_per_dispatch"] == pytest.approx(unit / 1e12) for r in per.values())
+    tot = recs[-1]
+    assert tot["calls"] == 2 and tot["executed_over_credited"] == pytest.approx(1.0)
+    assert tot["credited_tflop_per_call"] == pytest.approx(4 * unit / 1e12)
+    assert bench.summarize_mops(str(tmp_path), "tiny_f32", "single")[-1]["executed_over_credited"] == pytest.approx(4 / 3)
 
 
 def test_parse_sclk():
