@@ -854,6 +854,50 @@ def summarize_occupancy(csv_dir: str, min_us: float = 100.0) -> list[dict]:
     return out
 
 
+MEMSTALL_COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "TCC_HIT_sum", "TCC_MISS_sum",
+                     "TCP_TCC_READ_REQ_LATENCY_sum", "TCP_TCC_READ_REQ_sum", "TCP_PENDING_STALL_CYCLES_sum")
+
+
+def summarize_memstall(csv_dir: str, min_us: float = 100.0) -> list[dict]:
+    """Per kernel, from one rocprofv3 --pmc run of MEMSTALL_COUNTERS (csv, with each
+    dispatch's start and end): clock and MFMA busy as in summarize_occupancy, the L2 hit
+    rate, the mean latency of the L1's read requests to the L2 in cycles and in ns, and the
+    fraction of each CU's cycles in which its L1 held requests back because too many were
+    pending.  Kernels whose mean duration is under min_us are left out."""
+    import csv
+    import glob
+    import re
+    disp = {}
+    for p in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                d = disp.setdefault((p, r["Dispatch_Id"]), {
+                    "name": r["Kernel_Name"], "s": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    agg = {}
+    for d in disp.values():
+        if not all(c in d for c in MEMSTALL_COUNTERS):
+            continue
+        name = re.sub(r"\(anonymous namespace\)::|void ", "", d["name"]).split("(")[0].strip()
+        a = agg.setdefault(name, {c: 0.0 for c in MEMSTALL_COUNTERS + ("s", "n")})
+        a["n"] += 1
+        for c in MEMSTALL_COUNTERS + ("s",):
+            a[c] += d[c]
+    out = []
+    for name, a in agg.items():
+        if a["s"] / a["n"] * 1e6 < min_us:
+            continue
+        cyc = a["GRBM_GUI_ACTIVE"] / MI355X_XCDS
+        clk = cyc / a["s"] / 1e9
+        lat = a["TCP_TCC_READ_REQ_LATENCY_sum"] / max(a["TCP_TCC_READ_REQ_sum"], 1.0)
+        out.append({"kernel": name, "dispatches": int(a["n"]), "mean_us": a["s"] / a["n"] * 1e6, "clock_ghz": clk,
+                    "mfma_busy": a["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * MI355X_SIMDS),
+                    "l2_hit": a["TCC_HIT_sum"] / max(a["TCC_HIT_sum"] + a["TCC_MISS_sum"], 1.0),
+                    "l1_l2_read_latency_cycles": lat, "l1_l2_read_latency_ns": lat / clk,
+                    "l1_pending_stall": a["TCP_PENDING_STALL_CYCLES_sum"] / (cyc * MI355X_CUS)})
+    return out
+
+
 MOPS_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_F32")
 
 
@@ -924,6 +968,9 @@ def main() -> int:
     ap.add_argument("--summarize-occupancy", metavar="DIR",
                     help="only print, per kernel, clock, MFMA-busy and LDS figures from one rocprofv3 --pmc "
                          "run of bench.OCCUPANCY_COUNTERS under DIR; no GPU needed")
+    ap.add_argument("--summarize-memstall", metavar="DIR",
+                    help="only print, per kernel, L2 hit rate, L1-to-L2 read latency and L1 pending stalls "
+                         "from one rocprofv3 --pmc run of bench.MEMSTALL_COUNTERS under DIR; no GPU needed")
     ap.add_argument("--summarize-mops", metavar="DIR",
                     help="only print executed MFMA flops per kernel and per call, from one rocprofv3 --pmc run "
                          "of bench.MOPS_COUNTERS under DIR (--path, --workload name the run); no GPU needed")
@@ -937,6 +984,10 @@ def main() -> int:
         return 0
     if args.summarize_occupancy:
         for rec in summarize_occupancy(args.summarize_occupancy):
+            print(json.dumps(rec), flush=True)
+        return 0
+    if args.summarize_memstall:
+        for rec in summarize_memstall(args.summarize_memstall):
             print(json.dumps(rec), flush=True)
         return 0
     if args.summarize_mops:

@@ -169,6 +169,33 @@ def test_summarize_occupancy(tmp_path):
     assert r["lds_issue_wait"] == pytest.approx(0.1)
 
 
+def test_summarize_memstall(tmp_path):
+    """Two dispatches of 1 ms at 2.0 GHz: 80% L2 hits, 400 cycles (200 ns) per L1 read
+    request to the L2, pending stalls on a quarter of every CU's cycles; a dispatch missing
+    a counter is left out."""
+    cyc = 2e6
+    vals = {"GRBM_GUI_ACTIVE": 8 * cyc, "SQ_VALU_MFMA_BUSY_CYCLES": 0.6 * cyc * 1024, "TCC_HIT_sum": 800.0,
+            "TCC_MISS_sum": 200.0, "TCP_TCC_READ_REQ_LATENCY_sum": 400.0 * 5000, "TCP_TCC_READ_REQ_sum": 5000.0,
+            "TCP_PENDING_STALL_CYCLES_sum": 0.25 * cyc * 256}
+    assert set(vals) == set(bench.MEMSTALL_COUNTERS)
+    with open(tmp_path / "s_counter_collection.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp",
+                    "End_Timestamp"])
+        for d in range(2):
+            for c, v in vals.items():
+                w.writerow([d, "void (anonymous namespace)::gemm<bf16>(int)", c, v, 1000, 1_001_000])
+        w.writerow([2, "void (anonymous namespace)::gemm<bf16>(int)", "GRBM_GUI_ACTIVE", 1.0, 1000, 1_001_000])
+    recs = bench.summarize_memstall(str(tmp_path))
+    assert len(recs) == 1
+    r = recs[0]
+    assert (r["kernel"], r["dispatches"]) == ("gemm<bf16>", 2)
+    assert r["clock_ghz"] == pytest.approx(2.0) and r["mfma_busy"] == pytest.approx(0.6)
+    assert r["l2_hit"] == pytest.approx(0.8)
+    assert r["l1_l2_read_latency_cycles"] == pytest.approx(400.0) and r["l1_l2_read_latency_ns"] == pytest.approx(200.0)
+    assert r["l1_pending_stall"] == pytest.approx(0.25)
+
+
 def test_summarize_mops(tmp_path):
     """Two calls of the recomputing schedule at the tiny workload: per call a forward of
     2 N V D, a dz recompute of 2 N V D and two dH + dW launches of 2 N V D each (flops over
