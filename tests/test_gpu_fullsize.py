@@ -1,6 +1,6 @@
 """GPU parity at the full workload sizes (Llama-2, Mistral, Llama-3, Qwen-2.5 shaped heads
 in bf16, and the Llama-2 and Llama-3 heads in fp16), in the launch configuration the benchmark times
-(default workspace and chunking).
+(default workspace and chunking), and for a 256,000-token vocabulary whose W passes 2^31 bytes.
 
 Compared against fp64 oracle values stored by tests/golden/make_fullsize_golden.py:
 the loss, every row's lse, whole dH and dW rows at sampled positions (the head of the Zipf
@@ -119,4 +119,66 @@ def test_fullsize_bitwise_deterministic(name):
         assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a.view(torch.int16),
                            b.view(torch.int32) if b.dtype == torch.float32 else b.view(torch.int16))
     del outs
+    torch.cuda.empty_cache()
+
+
+def test_fullsize_wide_vocab():
+    """A 256,000-token vocabulary at D = 4608 (N = 1100, bf16): W spans 2.36 GB, so the last
+    89 of its 1000 vocabulary tiles start beyond 2 GiB into it.  The two calls with the
+    default workspace must match the stored oracle run (loss, every lse, dH and dW rows at
+    every tile edge) and keep the whole-output properties above.  The one-call entry point,
+    given a workspace far above any single pass's need, must decline the single pass (its
+    dH contraction over all of W would pass the kernels' 32-bit operand offsets) and give
+    the same bits as the two calls."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from linear_cross_entropy_lm_amd import binding as B
+    name = "wide_vocab_bf16"
+    cfg = I.GOLDEN_CASES[name]
+    print("case", cfg.describe(), flush=True)
+    gold = np.load(os.path.join(GOLDEN, f"fullsize_{name}.npz"))
+    inp = I.generate(cfg)
+    assert inp.digest() == str(gold["digest"]), "seeded inputs differ from the stored oracle run"
+    dev = "cuda:0"
+    H, W, y = inp.device_tensors(dev)
+    N, D, V = cfg.N, cfg.D, cfg.V
+    assert W.numel() * W.element_size() > 2**31
+    outs = {}
+    for entry in ("two_calls", "one_call"):
+        loss = torch.empty(1, dtype=torch.float32, device=dev)
+        lse = torch.empty(N, dtype=torch.float32, device=dev)
+        nv = torch.empty(1, dtype=torch.int32, device=dev)
+        st = torch.empty(1, dtype=torch.int32, device=dev)
+        dH = torch.full_like(H, float("nan"))
+        dW = torch.full((V, D), float("nan"), dtype=torch.float32, device=dev)
+        if entry == "two_calls":
+            ws = torch.empty(B.flce_workspace_bytes(N, D, V, H.dtype), dtype=torch.uint8, device=dev)
+            B.flce_forward(H, W, y, loss, lse, nv, st, ws, -100)
+            B.flce_backward(H, W, y, lse, nv, None, dH, dW, ws, -100)
+        else:
+            ws_bytes = 3 * 10**9
+            assert B.flce_forward_backward_chunk(N, D, V, H.dtype, ws_bytes) == 0
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+            B.flce_forward_backward(H, W, y, None, loss, lse, nv, st, dH, dW, ws)
+        torch.cuda.synchronize()
+        del ws
+        assert int(st.item()) == 0 and int(nv.item()) == int(gold["n_valid"])
+        outs[entry] = (loss, lse, dH, dW)
+    loss, lse, dH, dW = outs["two_calls"]
+    err = compare_golden(gold, loss, lse, dH, dW, cfg.dtype)
+    print(f"loss {loss.item():.6f} (oracle {float(gold['loss']):.6f}); errors {err}", flush=True)
+    for a, b in zip(outs["two_calls"], outs["one_call"]):
+        assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a.view(torch.int16),
+                           b.view(torch.int32) if b.dtype == torch.float32 else b.view(torch.int16))
+    del outs
+    assert bool(torch.isfinite(dH.float()).all()) and bool(torch.isfinite(dW).all())
+    assert bool((dH[y == -100] == 0).all())
+    colsum = dW.double().sum(dim=0).norm().item()
+    assert colsum <= 5e-3 * dW.double().norm().item()
+    lhs = (dW.double() * W.double()).sum().item()
+    rhs = (dH.double() * H.double()).sum().item()
+    print(f"|1^T dW| / |dW| {colsum / dW.double().norm().item():.2e}; <dW,W> vs <dH,H> rel "
+          f"{abs(lhs - rhs) / abs(lhs):.2e}", flush=True)
+    assert abs(lhs - rhs) <= 5e-4 * abs(lhs)
+    del dH, dW
     torch.cuda.empty_cache()
