@@ -103,11 +103,12 @@ GOLDEN_CASES = {
     # 16640 rows at the Qwen-2.5 vocabulary: one single-pass chunk of every row would span
     # 16640 x 152064 x 2 bytes, past 32-bit offsets, so the single pass runs capped chunks
     "spcap_bf16": case(16640, 64, 152064, "bf16", seed=1010),
-    # A 256,000-token vocabulary at a hidden size that puts the 16-bit W past 2^31 bytes
-    # (2.36 GB): the last 89 of its 1000 vocabulary tiles start beyond 2 GiB into W, and
-    # the single pass is unavailable (one dH contraction over all of W would pass the
-    # kernels' 32-bit operand offsets), so the one-call entry point runs the two calls
-    "wide_vocab_bf16": case(1100, 4608, 256000, "bf16", seed=1011),
+    # A 256,000-token vocabulary at a hidden size that puts W and dW past 2^31 elements
+    # (2.16e9; 4.33 GB in bf16, 8.65 GB in fp32): the last 503 of the 1000 vocabulary tiles
+    # start beyond 2 GiB into W and the last 7 beyond element 2^31, and the single pass is
+    # unavailable (one dH contraction over all of W would pass the kernels' 32-bit operand
+    # offsets), so the one-call entry point runs the two calls
+    "wide_vocab_bf16": case(1100, 8448, 256000, "bf16", seed=1011),
 }
 
 

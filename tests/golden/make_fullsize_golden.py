@@ -1,7 +1,7 @@
 """Write tests/golden/fullsize_<workload>.npz: fp64 oracle values for the full-size
 workloads (Llama-2, Mistral, Llama-3 and Qwen-2.5 shaped heads in bf16, Llama-2 and
-Llama-3 in fp16), for the capped single-pass case (spcap_bf16), for a vocabulary whose 16-bit
-W spans more than 2^31 bytes (wide_vocab_bf16), and for the cross-entropy over materialised
+Llama-3 in fp16), for the capped single-pass case (spcap_bf16), for a vocabulary whose W holds
+more than 2^31 elements (wide_vocab_bf16), and for the cross-entropy over materialised
 Llama-3-shaped logits (ce_llama3).
 
 Only the oracle and the seeded input generator are used.  Stored per workload:
