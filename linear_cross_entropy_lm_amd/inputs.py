@@ -109,6 +109,9 @@ GOLDEN_CASES = {
     # unavailable (one dH contraction over all of W would pass the kernels' 32-bit operand
     # offsets), so the one-call entry point runs the two calls
     "wide_vocab_bf16": case(1100, 8448, 256000, "bf16", seed=1011),
+    # Tokens rather than vocabulary past 2^31 elements: H and dH hold 262244 x 8448 = 2.2e9
+    # (4.4 GB in bf16), the last token tile ragged; here the single pass is available
+    "long_tokens_bf16": case(262244, 8448, 1031, "bf16", seed=1012),
 }
 
 

@@ -1,7 +1,7 @@
 """GPU parity at the full workload sizes (Llama-2, Mistral, Llama-3, Qwen-2.5 shaped heads
 in bf16, and the Llama-2 and Llama-3 heads in fp16), in the launch configuration the benchmark times
-(default workspace and chunking), and for a 256,000-token vocabulary whose W holds more than 2^31
-elements.
+(default workspace and chunking), and for W, dW (a 256,000-token vocabulary) or H, dH (262,244
+tokens) past 2^31 elements.
 
 Compared against fp64 oracle values stored by tests/golden/make_fullsize_golden.py:
 the loss, every row's lse, whole dH and dW rows at sampled positions (the head of the Zipf
@@ -123,19 +123,24 @@ def test_fullsize_bitwise_deterministic(name):
     torch.cuda.empty_cache()
 
 
-def test_fullsize_wide_vocab():
-    """A 256,000-token vocabulary at D = 8448 (N = 1100, bf16): W and dW hold 2.16e9 elements
-    (4.33 GB and 8.65 GB), so the last 503 of the 1000 vocabulary tiles start beyond 2 GiB
-    into W and the last 7 beyond element 2^31.  The two calls with the
-    default workspace must match the stored oracle run (loss, every lse, dH and dW rows at
-    every tile edge) and keep the whole-output properties above.  The one-call entry point,
-    given a workspace far above any single pass's need, must decline the single pass (its
-    dH contraction over all of W would pass the kernels' 32-bit operand offsets) and give
-    the same bits as the two calls."""
+@pytest.mark.parametrize("name", ["wide_vocab_bf16", "long_tokens_bf16"])
+def test_fullsize_past_2e31_elements(name):
+    """Operands past 2^31 elements, against the stored oracle run (loss, every lse, dH and
+    dW rows at every tile edge) and the whole-output properties above.
+
+    wide_vocab_bf16: a 256,000-token vocabulary at D = 8448 (N = 1100): W and dW hold 2.16e9
+    elements (4.33 GB and 8.65 GB), so the last 503 of the 1000 vocabulary tiles start
+    beyond 2 GiB into W and the last 7 beyond element 2^31.  The one-call entry point, given
+    a workspace far above any single pass's need, must decline the single pass (its dH
+    contraction over all of W would pass the kernels' 32-bit operand offsets) and give the
+    same bits as the two calls.
+
+    long_tokens_bf16: 262,244 tokens at D = 8448 (V = 1031): H and dH hold 2.2e9 elements.
+    The one-call entry point with the single pass's least workspace runs the single pass in
+    65 token chunks and must match the oracle too."""
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     from linear_cross_entropy_lm_amd import binding as B
-    name = "wide_vocab_bf16"
     cfg = I.GOLDEN_CASES[name]
     print("case", cfg.describe(), flush=True)
     gold = np.load(os.path.join(GOLDEN, f"fullsize_{name}.npz"))
@@ -144,7 +149,7 @@ def test_fullsize_wide_vocab():
     dev = "cuda:0"
     H, W, y = inp.device_tensors(dev)
     N, D, V = cfg.N, cfg.D, cfg.V
-    assert W.numel() > 2**31
+    assert max(H.numel(), W.numel()) > 2**31
     outs = {}
     for entry in ("two_calls", "one_call"):
         loss = torch.empty(1, dtype=torch.float32, device=dev)
@@ -158,34 +163,40 @@ def test_fullsize_wide_vocab():
             B.flce_forward(H, W, y, loss, lse, nv, st, ws, -100)
             B.flce_backward(H, W, y, lse, nv, None, dH, dW, ws, -100)
         else:
-            ws_bytes = 3 * 10**9
-            assert B.flce_forward_backward_chunk(N, D, V, H.dtype, ws_bytes) == 0
+            if name == "wide_vocab_bf16":
+                ws_bytes = 3 * 10**9
+                assert B.flce_forward_backward_chunk(N, D, V, H.dtype, ws_bytes) == 0
+            else:
+                ws_bytes = B.flce_forward_backward_workspace_bytes(N, D, V, H.dtype)
+                assert B.flce_forward_backward_chunk(N, D, V, H.dtype, ws_bytes) == 4096
             ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
             B.flce_forward_backward(H, W, y, None, loss, lse, nv, st, dH, dW, ws)
         torch.cuda.synchronize()
         del ws
         assert int(st.item()) == 0 and int(nv.item()) == int(gold["n_valid"])
+        err = compare_golden(gold, loss, lse, dH, dW, cfg.dtype)
+        print(f"{entry}: loss {loss.item():.6f} (oracle {float(gold['loss']):.6f}); errors {err}", flush=True)
         outs[entry] = (loss, lse, dH, dW)
+    if name == "wide_vocab_bf16":
+        for a, b in zip(outs["two_calls"], outs["one_call"]):
+            assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a.view(torch.int16),
+                               b.view(torch.int32) if b.dtype == torch.float32 else b.view(torch.int16))
     loss, lse, dH, dW = outs["two_calls"]
-    err = compare_golden(gold, loss, lse, dH, dW, cfg.dtype)
-    print(f"loss {loss.item():.6f} (oracle {float(gold['loss']):.6f}); errors {err}", flush=True)
-    for a, b in zip(outs["two_calls"], outs["one_call"]):
-        assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a.view(torch.int16),
-                           b.view(torch.int32) if b.dtype == torch.float32 else b.view(torch.int16))
     del outs
     assert bool(torch.isfinite(dH.float()).all()) and bool(torch.isfinite(dW).all())
     assert bool((dH[y == -100] == 0).all())
-    # the whole-output properties in fp64, over blocks of vocabulary rows
+    # the whole-output properties in fp64, over blocks of rows
     col = torch.zeros(D, dtype=torch.float64, device=dev)
-    sq = lhs = 0.0
+    sq = lhs = rhs = 0.0
     for v0 in range(0, V, 16384):
         blk = dW[v0:v0 + 16384].double()
         col += blk.sum(dim=0)
         sq += (blk * blk).sum().item()
         lhs += (blk * W[v0:v0 + 16384].double()).sum().item()
         del blk
+    for n0 in range(0, N, 16384):
+        rhs += (dH[n0:n0 + 16384].double() * H[n0:n0 + 16384].double()).sum().item()
     colsum, norm = col.norm().item(), sq ** 0.5
-    rhs = (dH.double() * H.double()).sum().item()
     print(f"|1^T dW| / |dW| {colsum / norm:.2e}; <dW,W> vs <dH,H> rel {abs(lhs - rhs) / abs(lhs):.2e}", flush=True)
     assert colsum <= 5e-3 * norm
     assert abs(lhs - rhs) <= 5e-4 * abs(lhs)
