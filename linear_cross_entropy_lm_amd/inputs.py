@@ -112,6 +112,9 @@ GOLDEN_CASES = {
     # Tokens rather than vocabulary past 2^31 elements: H and dH hold 262244 x 8448 = 2.2e9
     # (4.4 GB in bf16), the last token tile ragged; here the single pass is available
     "long_tokens_bf16": case(262244, 8448, 1031, "bf16", seed=1012),
+    # The Llama-3-shaped head with fp32 inputs: W and dW are 2.1 GB each, and the single
+    # pass's dH contraction over all of W stays just inside the 32-bit operand offsets
+    "llama3_f32": replace(CONFIGS["llama3"], name="llama3_f32", dtype="f32", seed=1013),
 }
 
 

@@ -1,7 +1,8 @@
 """Write tests/golden/fullsize_<workload>.npz: fp64 oracle values for the full-size
 workloads (Llama-2, Mistral, Llama-3 and Qwen-2.5 shaped heads in bf16, Llama-2 and
 Llama-3 in fp16), for the capped single-pass case (spcap_bf16), for a vocabulary whose W holds
-more than 2^31 elements (wide_vocab_bf16), for as many tokens in H (long_tokens_bf16), and for the cross-entropy over materialised
+more than 2^31 elements (wide_vocab_bf16), for as many tokens in H (long_tokens_bf16), for the
+Llama-3-shaped head with fp32 inputs (llama3_f32), and for the cross-entropy over materialised
 Llama-3-shaped logits (ce_llama3).
 
 Only the oracle and the seeded input generator are used.  Stored per workload:
@@ -41,7 +42,7 @@ import oracle  # noqa: E402
 from linear_cross_entropy_lm_amd import inputs as I  # noqa: E402
 
 WORKLOADS = ["llama2", "mistral", "llama3", "qwen25", "llama2_f16", "llama3_f16", "spcap_bf16", "wide_vocab_bf16",
-             "long_tokens_bf16", "ce_llama3", "chain_llama3"]
+             "long_tokens_bf16", "llama3_f32", "ce_llama3", "chain_llama3"]
 TILE = 256
 
 
