@@ -33,6 +33,11 @@ roofline     the kernel kind with the largest share of the step: its algorithmic
              kernel source, else null
 cpu_baseline the fp64 oracle timed on this host's cores on the first R rows of the same
              workload (full vocabulary and hidden size), scaled to tokens/s
+
+Modes that only read rocprofv3 output and need no GPU: --summarize-trace (per-kernel
+durations), --summarize-counters (HBM traffic records), --summarize-occupancy (clock,
+MFMA busy, LDS), --summarize-memstall (L2 hits, L1-to-L2 read latency, L1 pending stalls),
+--summarize-mops (executed MFMA flops against the credited ones).
 """
 from __future__ import annotations
 
