@@ -810,6 +810,29 @@ def summarize_trace(path: str) -> list[dict]:
     return sorted(out, key=lambda r: -r["share"])
 
 
+def _counter_dispatches(csv_dir: str) -> list[dict]:
+    """Every dispatch in the rocprofv3 --pmc csv output under csv_dir: the kernel's short
+    name, its grid and workgroup sizes and its duration in seconds ("s") where the rows
+    carry them, and each counter summed over the rows (instances) that report it."""
+    import csv
+    import glob
+    import re
+    disp = {}
+    for path in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                d = disp.get((path, r["Dispatch_Id"]))
+                if d is None:
+                    d = {"name": re.sub(r"\(anonymous namespace\)::|void ", "", r["Kernel_Name"]).split("(")[0].strip()}
+                    if r.get("Grid_Size"):
+                        d["grid"], d["wg"] = int(r["Grid_Size"]), int(r["Workgroup_Size"])
+                    if r.get("Start_Timestamp"):
+                        d["s"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+                    disp[(path, r["Dispatch_Id"])] = d
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return list(disp.values())
+
+
 OCCUPANCY_COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT",
                       "SQ_LDS_ADDR_CONFLICT", "SQ_BUSY_CU_CYCLES", "SQ_WAIT_INST_LDS", "SQ_LDS_DATA_FIFO_FULL")
 MI355X_XCDS, MI355X_CUS, MI355X_SIMDS = 8, 256, 1024
@@ -823,24 +846,11 @@ def summarize_occupancy(csv_dir: str, min_us: float = 100.0) -> list[dict]:
     product clock x MFMA busy (GHz of fully busy MFMA issue), and the LDS-active, LDS
     bank-conflict and LDS-issue-wait fractions (per CU, per CU, per SIMD; the wait counter is
     in units of 4 cycles).  Kernels whose mean duration is under min_us are left out."""
-    import csv
-    import glob
-    import re
-    disp = {}
-    for path in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
-        with open(path) as f:
-            for r in csv.DictReader(f):
-                key = (path, r["Dispatch_Id"])
-                d = disp.setdefault(key, {"name": r["Kernel_Name"], "grid": int(r["Grid_Size"]),
-                                          "wg": int(r["Workgroup_Size"]),
-                                          "s": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9})
-                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
     agg = {}
-    for d in disp.values():
+    for d in _counter_dispatches(csv_dir):
         if not all(c in d for c in OCCUPANCY_COUNTERS):
             continue
-        name = re.sub(r"\(anonymous namespace\)::|void ", "", d["name"]).split("(")[0].strip()
-        a = agg.setdefault((name, d["grid"] // d["wg"], d["wg"]), {c: 0.0 for c in OCCUPANCY_COUNTERS + ("s", "n")})
+        a = agg.setdefault((d["name"], d["grid"] // d["wg"], d["wg"]), {c: 0.0 for c in OCCUPANCY_COUNTERS + ("s", "n")})
         a["n"] += 1
         for c in OCCUPANCY_COUNTERS + ("s",):
             a[c] += d[c]
@@ -869,22 +879,11 @@ def summarize_memstall(csv_dir: str, min_us: float = 100.0) -> list[dict]:
     rate, the mean latency of the L1's read requests to the L2 in cycles and in ns, and the
     fraction of each CU's cycles in which its L1 held requests back because too many were
     pending.  Kernels whose mean duration is under min_us are left out."""
-    import csv
-    import glob
-    import re
-    disp = {}
-    for p in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
-        with open(p) as f:
-            for r in csv.DictReader(f):
-                d = disp.setdefault((p, r["Dispatch_Id"]), {
-                    "name": r["Kernel_Name"], "s": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9})
-                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
     agg = {}
-    for d in disp.values():
+    for d in _counter_dispatches(csv_dir):
         if not all(c in d for c in MEMSTALL_COUNTERS):
             continue
-        name = re.sub(r"\(anonymous namespace\)::|void ", "", d["name"]).split("(")[0].strip()
-        a = agg.setdefault(name, {c: 0.0 for c in MEMSTALL_COUNTERS + ("s", "n")})
+        a = agg.setdefault(d["name"], {c: 0.0 for c in MEMSTALL_COUNTERS + ("s", "n")})
         a["n"] += 1
         for c in MEMSTALL_COUNTERS + ("s",):
             a[c] += d[c]
@@ -913,25 +912,12 @@ def summarize_mops(csv_dir: str, workload: str, path: str = "fused") -> list[dic
     of the path (the calls are counted by fwd_finalize, launched once per forward or
     one-call pass), set against the flops the path is credited with: 8 N V D for the
     recomputing schedule (forward, dz recompute, dH, dW), 6 N V D for the single pass."""
-    import csv
-    import glob
-    import re
-
     from linear_cross_entropy_lm_amd import inputs as I
-    disp = {}
-    for p in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
-        with open(p) as f:
-            for r in csv.DictReader(f):
-                if r["Counter_Name"] not in MOPS_COUNTERS:
-                    continue
-                d = disp.setdefault((p, r["Dispatch_Id"]), {"name": r["Kernel_Name"], "flop": 0.0})
-                d["flop"] += 512.0 * float(r["Counter_Value"])
     per = {}
-    for d in disp.values():
-        name = re.sub(r"\(anonymous namespace\)::|void ", "", d["name"]).split("(")[0].strip()
-        a = per.setdefault(name, {"dispatches": 0, "flop": 0.0})
+    for d in _counter_dispatches(csv_dir):
+        a = per.setdefault(d["name"], {"dispatches": 0, "flop": 0.0})
         a["dispatches"] += 1
-        a["flop"] += d["flop"]
+        a["flop"] += 512.0 * sum(d.get(c, 0.0) for c in MOPS_COUNTERS)
     calls = sum(a["dispatches"] for n, a in per.items() if n.startswith("fwd_finalize"))
     out = [{"kernel": n, "dispatches": a["dispatches"], "tflop_per_dispatch": a["flop"] / a["dispatches"] / 1e12}
            for n, a in sorted(per.items(), key=lambda kv: -kv[1]["flop"]) if a["flop"] > 0]
