@@ -171,6 +171,35 @@ def test_custom_ignore_index_and_upstream_grad(dtype):
     compare(got, ref, dtype)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_zero_upstream_grad_gives_exact_zeros(dtype):
+    """g = 0: every row's scale g / N_valid is 0, so dz, dH and dW are exactly zero (no 0/0
+    in the fp16 slab's scaling), through the two calls and through the single pass; the
+    forward's loss and lse are unaffected."""
+    from linear_cross_entropy_lm_amd import binding as B
+    cfg = I.case(520, 256, 1031, dtype, seed=52)
+    inp = I.generate(cfg)
+    ref = _oracle(inp)
+    got = run_gpu(inp, g=0.0)
+    compare(got, ref, dtype, grads=False)
+    assert not np.any(got["dH"]) and not np.any(got["dW"])
+    H, W, y = inp.device_tensors("cuda:0")
+    N, D, V = cfg.N, cfg.D, cfg.V
+    ws = torch.empty(B.flce_forward_backward_workspace_bytes(N, D, V, H.dtype), dtype=torch.uint8, device="cuda:0")
+    loss = torch.empty(1, dtype=torch.float32, device="cuda:0")
+    lse = torch.empty(N, dtype=torch.float32, device="cuda:0")
+    nv = torch.empty(1, dtype=torch.int32, device="cuda:0")
+    st = torch.empty(1, dtype=torch.int32, device="cuda:0")
+    dH = torch.full_like(H, float("nan"))
+    dW = torch.full((V, D), float("nan"), dtype=torch.float32, device="cuda:0")
+    g = torch.zeros(1, dtype=torch.float32, device="cuda:0")
+    B.flce_forward_backward(H, W, y, g, loss, lse, nv, st, dH, dW, ws)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert abs(loss.item() - ref["loss"]) <= 2e-3 * abs(ref["loss"])
+    assert bool((dH == 0).all()) and bool((dW == 0).all())
+
+
 def test_bitwise_deterministic():
     cfg = I.case(700, 384, 3000, "bf16", seed=46)
     inp = I.generate(cfg)
